@@ -1,0 +1,69 @@
+"""Build libtq.so (HIP, gfx950) in-tree with hipcc.
+
+Flags that the bit-exact results depend on:
+  -ffp-contract=off                          no fused multiply-add contraction
+  -fno-gpu-flush-denormals-to-zero           binary32 subnormals are kept
+  -fhip-fp32-correctly-rounded-divide-sqrt   IEEE-rounded division
+  -Xclang -target-feature -Xclang -packed-fp32-ops
+                                             no packed-fp32 instructions
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libtq.so")
+BUILD_DIR = os.path.join(HERE, "_build")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+
+SOURCES = ["tq_api.cpp", "tq_quantize.hip", "tq_sr.hip", "tq_gemm.hip"]
+
+COMMON = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+    "-ffp-contract=off", "-fno-gpu-flush-denormals-to-zero",
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fvisibility=hidden", "-Wall", "-Wno-unused-command-line-argument",
+]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libtq.so; always rebuilds."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+def asm(src: str) -> str:
+    """Device assembly of one source (for inspecting the generated gfx950 code)."""
+    cmd = [HIPCC, *COMMON, "-x", "hip", "--cuda-device-only", "-S",
+           os.path.join(CSRC, src), "-o", "-"]
+    return subprocess.run(cmd, capture_output=True, text=True, check=True).stdout
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

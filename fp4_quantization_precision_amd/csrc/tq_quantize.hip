@@ -1,0 +1,456 @@
+// tq_quantize.hip - bandwidth-bound kernels of the FP4 path for gfx950:
+// tensor amax, nearest / guided NVFP4 quantization (with the fused 1-bit hint),
+// standalone hint extraction, dequantization and code-mismatch counting.
+//
+// Layout and arithmetic follow include/tq.h.  Each lane owns whole 16-element
+// blocks, so a block's maximum, its E4M3 scale and its reciprocal stay in the
+// lane's registers with no cross-lane reduction; a wave covers 64 consecutive
+// blocks (2 KiB of bf16), its loads are 16-byte vectors and its stores are one
+// 8-byte code word, one scale byte and one 16-bit hint word per lane.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq_device.hpp"
+#include "tq_kernels.hpp"
+
+namespace tq {
+
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------------------
+// small fills (used instead of memset nodes, which misbehave under graph replay)
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kThreads) void fill_u32_kernel(uint32_t* __restrict__ p, uint32_t v,
+                                                            int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * kThreads)
+        p[i] = v;
+}
+
+void launch_fill_u32(uint32_t* p, uint32_t v, int64_t n, hipStream_t s)
+{
+    if (n <= 0)
+        return;
+    int64_t g = (n + kThreads - 1) / kThreads;
+    if (g > 1024)
+        g = 1024;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)g), dim3(kThreads), 0, s, p, v, n);
+}
+
+// ---------------------------------------------------------------------------
+// tensor amax
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
+        v = v > o ? v : o;
+    }
+    return v;
+}
+
+__device__ __forceinline__ uint32_t abs_bits_max(uint4 q, bool bf16, uint32_t m)
+{
+    uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (bf16) {
+            uint32_t lo = (w[i] << 16) & 0x7FFF0000u;
+            uint32_t hi = w[i] & 0x7FFF0000u;
+            m = m > lo ? m : lo;
+            m = m > hi ? m : hi;
+        } else {
+            uint32_t a = w[i] & 0x7FFFFFFFu;
+            m = m > a ? m : a;
+        }
+    }
+    return m;
+}
+
+// |x| of finite binary32 values orders like the unsigned integer of its bits,
+// so the maximum is taken on bit patterns and published with an integer atomic.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict__ x,
+                                                        int64_t vec_per_tensor, int64_t batch,
+                                                        float* __restrict__ amax)
+{
+    __shared__ uint32_t red[kThreads / 64];
+    for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
+        const uint4* xb = x + b * vec_per_tensor;
+        uint32_t m = 0;
+        int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+        const int64_t stride = (int64_t)gridDim.x * kThreads;
+        for (; i + 3 * stride < vec_per_tensor; i += 4 * stride) {
+            uint4 q0 = xb[i], q1 = xb[i + stride], q2 = xb[i + 2 * stride],
+                  q3 = xb[i + 3 * stride];
+            m = abs_bits_max(q0, BF16, m);
+            m = abs_bits_max(q1, BF16, m);
+            m = abs_bits_max(q2, BF16, m);
+            m = abs_bits_max(q3, BF16, m);
+        }
+        for (; i < vec_per_tensor; i += stride)
+            m = abs_bits_max(xb[i], BF16, m);
+        m = wave_max_u32(m);
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        if (lane == 0)
+            red[wave] = m;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t r = red[0];
+#pragma unroll
+            for (int w = 1; w < kThreads / 64; ++w)
+                r = r > red[w] ? r : red[w];
+            if (r != 0)
+                atomicMax(reinterpret_cast<unsigned int*>(amax + b), r);
+        }
+        __syncthreads();
+    }
+}
+
+static unsigned grid_y(int64_t batch) { return (unsigned)(batch < 65535 ? batch : 65535); }
+
+// Workgroups per tensor so that the whole launch has about `target` groups.
+static unsigned groups_per_tensor(int64_t work_items, int64_t batch, int64_t target)
+{
+    int64_t need = (work_items + kThreads - 1) / kThreads;
+    int64_t cap = target / (batch < 1 ? 1 : batch);
+    if (cap < 1)
+        cap = 1;
+    int64_t g = need < cap ? need : cap;
+    return (unsigned)(g < 1 ? 1 : g);
+}
+
+void launch_amax(const void* x, bool bf16, int64_t batch, int64_t per_tensor, float* amax,
+                 hipStream_t s)
+{
+    launch_fill_u32(reinterpret_cast<uint32_t*>(amax), 0u, batch, s);
+    const int64_t vec = per_tensor * (bf16 ? 2 : 4) / 16;
+    if (vec == 0)
+        return;
+    dim3 grid(groups_per_tensor(vec / 4, batch, 4096), grid_y(batch));
+    if (bf16)
+        hipLaunchKernelGGL(amax_kernel<true>, grid, dim3(kThreads), 0, s,
+                           static_cast<const uint4*>(x), vec, batch, amax);
+    else
+        hipLaunchKernelGGL(amax_kernel<false>, grid, dim3(kThreads), 0, s,
+                           static_cast<const uint4*>(x), vec, batch, amax);
+}
+
+// ---------------------------------------------------------------------------
+// nearest / guided quantization
+// ---------------------------------------------------------------------------
+
+enum { MODE_NEAREST = kModeNearest, MODE_NEAREST_HINT = kModeNearestHint, MODE_GUIDED = kModeGuided };
+
+template <bool BF16>
+__device__ __forceinline__ void load_block(const void* __restrict__ x, int64_t blk, float v[16])
+{
+    if (BF16) {
+        const uint4* p = static_cast<const uint4*>(x) + 2 * blk;
+        uint4 a = p[0], b = p[1];
+        uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            v[2 * i] = bf16_lo(w[i]);
+            v[2 * i + 1] = bf16_hi(w[i]);
+        }
+    } else {
+        const float4* p = static_cast<const float4*>(x) + 4 * blk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float4 q = p[i];
+            v[4 * i] = q.x;
+            v[4 * i + 1] = q.y;
+            v[4 * i + 2] = q.z;
+            v[4 * i + 3] = q.w;
+        }
+    }
+}
+
+// One lane quantizes one 16-element block: amax -> E4M3 scale -> reciprocal ->
+// 16 codes, packed 8 bytes; MODE_NEAREST_HINT also emits the 16 parity bits and
+// MODE_GUIDED consumes them.
+template <bool BF16, int MODE>
+__global__ __launch_bounds__(kThreads) void quantize_kernel(
+    const void* __restrict__ x, int64_t blocks_per_tensor, int64_t batch,
+    const float* __restrict__ tensor_amax, uint2* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ tensor_scale,
+    uint16_t* __restrict__ hints, int64_t total_blocks)
+{
+    for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
+        const float A_T = tensor_amax[b];
+        const float s_t = (A_T == 0.0f) ? 0.0f : A_T / 2688.0f;
+        if (blockIdx.x == 0 && threadIdx.x == 0)
+            tensor_scale[b] = s_t;
+        for (int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x; j < blocks_per_tensor;
+             j += (int64_t)gridDim.x * kThreads) {
+            const int64_t blk = b * blocks_per_tensor + j;
+            float v[16];
+            load_block<BF16>(x, blk, v);
+            uint32_t hin = 0;
+            if (MODE == MODE_GUIDED)
+                hin = hints[blk];
+            float A_b = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                A_b = fmaxf(A_b, fabsf(v[i]));
+            uint32_t e = 0;
+            if (s_t != 0.0f)
+                e = e4m3_encode((A_b / 6.0f) / s_t);
+            const float dec = e4m3_decode(e);
+            uint32_t lo = 0, hi = 0, par = 0;
+            if (dec != 0.0f) {
+                const float r_b = 1.0f / (dec * s_t);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float y = v[i] * r_b;
+                    const float a = fabsf(y);
+                    uint32_t m;
+                    if (MODE == MODE_GUIDED)
+                        m = e2m1_guided(a, (hin >> i) & 1u);
+                    else
+                        m = e2m1_nearest(a);
+                    const uint32_t c = e2m1_code(y, m);
+                    if (i < 8)
+                        lo |= c << (4 * i);
+                    else
+                        hi |= c << (4 * (i - 8));
+                    par |= (m & 1u) << i;
+                }
+            }
+            codes[blk] = make_uint2(lo, hi);
+            scales[blk] = (uint8_t)e;
+            if (MODE == MODE_NEAREST_HINT) {
+                hints[blk] = (uint16_t)par;
+                if ((total_blocks & 1) && blk == total_blocks - 1)
+                    hints[blk + 1] = 0;  // zero the unused half of the last word
+            }
+        }
+    }
+}
+
+void launch_quantize(const void* x, bool bf16, int64_t batch, int64_t rows, int64_t cols,
+                     const float* tensor_amax, uint8_t* codes, uint8_t* scales,
+                     float* tensor_scale, uint32_t* hints, int mode, hipStream_t s)
+{
+    const int64_t bpt = rows * cols / 16;
+    const int64_t total = bpt * batch;
+    dim3 grid(groups_per_tensor(bpt, batch, 4096), grid_y(batch));
+    uint2* c2 = reinterpret_cast<uint2*>(codes);
+    uint16_t* h = reinterpret_cast<uint16_t*>(hints);
+#define TQ_QLAUNCH(B, M)                                                                     \
+    hipLaunchKernelGGL((quantize_kernel<B, M>), grid, dim3(kThreads), 0, s, x, bpt, batch,   \
+                       tensor_amax, c2, scales, tensor_scale, h, total)
+    if (bf16) {
+        if (mode == MODE_NEAREST)
+            TQ_QLAUNCH(true, MODE_NEAREST);
+        else if (mode == MODE_NEAREST_HINT)
+            TQ_QLAUNCH(true, MODE_NEAREST_HINT);
+        else
+            TQ_QLAUNCH(true, MODE_GUIDED);
+    } else {
+        if (mode == MODE_NEAREST)
+            TQ_QLAUNCH(false, MODE_NEAREST);
+        else if (mode == MODE_NEAREST_HINT)
+            TQ_QLAUNCH(false, MODE_NEAREST_HINT);
+        else
+            TQ_QLAUNCH(false, MODE_GUIDED);
+    }
+#undef TQ_QLAUNCH
+}
+
+// Per-tensor scalars of empty tensors: amax (unless given) and tensor scale are 0.
+__global__ void empty_tensor_scalars_kernel(float* amax, float* ts, int64_t batch, int write_amax)
+{
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < batch;
+         b += (int64_t)gridDim.x * blockDim.x) {
+        if (write_amax)
+            amax[b] = 0.0f;
+        ts[b] = 0.0f;
+    }
+}
+
+void launch_empty_tensor_scalars(float* amax, float* ts, int64_t batch, bool write_amax,
+                                 hipStream_t s)
+{
+    if (batch <= 0)
+        return;
+    hipLaunchKernelGGL(empty_tensor_scalars_kernel, dim3(1), dim3(kThreads), 0, s, amax, ts, batch,
+                       write_amax ? 1 : 0);
+}
+
+// ---------------------------------------------------------------------------
+// standalone hint extraction: word w <- parity bits of codes 32w .. 32w+31
+// ---------------------------------------------------------------------------
+
+// Gather bits 0, 4, 8, ..., 28 of w into bits 0..7.
+__device__ __forceinline__ uint32_t gather_nibble_lsbs(uint32_t w)
+{
+    uint32_t x = w & 0x11111111u;
+    x = (x | (x >> 3)) & 0x03030303u;
+    x = (x | (x >> 6)) & 0x000F000Fu;
+    x = (x | (x >> 12)) & 0x000000FFu;
+    return x;
+}
+
+__global__ __launch_bounds__(kThreads) void extract_hint_kernel(const uint8_t* __restrict__ codes,
+                                                                int64_t n,
+                                                                uint32_t* __restrict__ hints,
+                                                                int64_t words)
+{
+    for (int64_t w = (int64_t)blockIdx.x * kThreads + threadIdx.x; w < words;
+         w += (int64_t)gridDim.x * kThreads) {
+        uint32_t bits = 0;
+        if (32 * w + 32 <= n) {
+            uint4 q = reinterpret_cast<const uint4*>(codes)[w];
+            bits = gather_nibble_lsbs(q.x) | (gather_nibble_lsbs(q.y) << 8) |
+                   (gather_nibble_lsbs(q.z) << 16) | (gather_nibble_lsbs(q.w) << 24);
+        } else {
+            const int64_t nbytes = (n + 1) / 2;
+            for (int j = 0; j < 16 && 16 * w + j < nbytes; ++j) {
+                uint32_t byte = codes[16 * w + j];
+                bits |= (byte & 1u) << (2 * j);
+                bits |= ((byte >> 4) & 1u) << (2 * j + 1);
+            }
+            const int64_t valid = n - 32 * w;  // 1..31
+            bits &= (1u << valid) - 1u;
+        }
+        hints[w] = bits;
+    }
+}
+
+void launch_extract_hint(const uint8_t* codes, int64_t n, uint32_t* hints, hipStream_t s)
+{
+    const int64_t words = (n + 31) / 32;
+    if (words == 0)
+        return;
+    int64_t g = (words + kThreads - 1) / kThreads;
+    if (g > 8192)
+        g = 8192;
+    hipLaunchKernelGGL(extract_hint_kernel, dim3((unsigned)g), dim3(kThreads), 0, s, codes, n,
+                       hints, words);
+}
+
+// ---------------------------------------------------------------------------
+// dequantization: one lane per 16-element block
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(kThreads) void dequantize_kernel(const uint2* __restrict__ codes,
+                                                              const uint8_t* __restrict__ scales,
+                                                              const float* __restrict__ ts,
+                                                              int64_t blocks_per_tensor,
+                                                              int64_t batch,
+                                                              float4* __restrict__ out)
+{
+    for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
+        const float s_t = ts[b];
+        for (int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x; j < blocks_per_tensor;
+             j += (int64_t)gridDim.x * kThreads) {
+            const int64_t blk = b * blocks_per_tensor + j;
+            const uint2 c = codes[blk];
+            const float d = e4m3_decode(scales[blk]);
+            float v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const uint32_t code = ((i < 8 ? c.x : c.y) >> (4 * (i & 7))) & 15u;
+                const float mag = (e2m1_value(code & 7u) * d) * s_t;
+                v[i] = (code & 8u) ? -mag : mag;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                out[4 * blk + i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+        }
+    }
+}
+
+void launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* ts, int64_t batch,
+                       int64_t rows, int64_t cols, float* out, hipStream_t s)
+{
+    const int64_t bpt = rows * cols / 16;
+    dim3 grid(groups_per_tensor(bpt, batch, 4096), grid_y(batch));
+    hipLaunchKernelGGL(dequantize_kernel, grid, dim3(kThreads), 0, s,
+                       reinterpret_cast<const uint2*>(codes), scales, ts, bpt, batch,
+                       reinterpret_cast<float4*>(out));
+}
+
+// ---------------------------------------------------------------------------
+// code mismatch counting
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int signed_pos(uint32_t c)
+{
+    const int m = (int)(c & 7u);
+    return (c & 8u) ? -m : m;
+}
+
+__device__ __forceinline__ void count_word(uint32_t a, uint32_t b, uint32_t& mism, uint32_t& adj)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t ca = (a >> (4 * i)) & 15u, cb = (b >> (4 * i)) & 15u;
+        const int d = signed_pos(ca) - signed_pos(cb);
+        mism += (ca != cb) ? 1u : 0u;
+        adj += (d == 1 || d == -1) ? 1u : 0u;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void mismatch_kernel(const uint4* __restrict__ a,
+                                                            const uint4* __restrict__ b,
+                                                            int64_t vec_per_tensor, int64_t batch,
+                                                            unsigned long long* __restrict__ counts)
+{
+    __shared__ uint32_t red[2][kThreads / 64];
+    for (int64_t t = blockIdx.y; t < batch; t += gridDim.y) {
+        uint32_t mism = 0, adj = 0;
+        for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < vec_per_tensor;
+             i += (int64_t)gridDim.x * kThreads) {
+            const uint4 qa = a[t * vec_per_tensor + i], qb = b[t * vec_per_tensor + i];
+            count_word(qa.x, qb.x, mism, adj);
+            count_word(qa.y, qb.y, mism, adj);
+            count_word(qa.z, qb.z, mism, adj);
+            count_word(qa.w, qb.w, mism, adj);
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            mism += (uint32_t)__shfl_xor((int)mism, off, 64);
+            adj += (uint32_t)__shfl_xor((int)adj, off, 64);
+        }
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        if (lane == 0) {
+            red[0][wave] = mism;
+            red[1][wave] = adj;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            unsigned long long m = 0, d = 0;
+            for (int w = 0; w < kThreads / 64; ++w) {
+                m += red[0][w];
+                d += red[1][w];
+            }
+            if (m)
+                atomicAdd(counts + 2 * t, m);
+            if (d)
+                atomicAdd(counts + 2 * t + 1, d);
+        }
+        __syncthreads();
+    }
+}
+
+void launch_mismatch(const uint8_t* a, const uint8_t* b, int64_t batch, int64_t per_tensor,
+                     uint64_t* counts, hipStream_t s)
+{
+    launch_fill_u32(reinterpret_cast<uint32_t*>(counts), 0u, 4 * batch, s);
+    const int64_t vec = per_tensor / 32;
+    if (vec == 0)
+        return;
+    dim3 grid(groups_per_tensor(vec, batch, 2048), grid_y(batch));
+    hipLaunchKernelGGL(mismatch_kernel, grid, dim3(kThreads), 0, s,
+                       reinterpret_cast<const uint4*>(a), reinterpret_cast<const uint4*>(b), vec,
+                       batch, reinterpret_cast<unsigned long long*>(counts));
+}
+
+}  // namespace tq

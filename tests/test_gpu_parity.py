@@ -1,0 +1,477 @@
+"""GPU parity: libtq (HIP, through the C ABI) against the CPU oracle on the same
+seeded inputs.  Codes, scales, tensor scales, hints, stochastic-rounding outputs,
+dequantized values and counters must match bit for bit; the grouped GEMM must
+satisfy |gpu - ref| <= 1e-3 * sum_k |a*w| for every checked output.
+
+Full-size workloads are checked on samples the oracle computes one by one
+(whole expert tensors, sampled token rows, sampled GEMM rows); small cases are
+checked element by element.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp4_quantization_precision_amd import inputs, ops
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda")
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def npu8(t):
+    return t.detach().cpu().contiguous().numpy().reshape(-1)
+
+
+def hints_np(t):
+    return t.detach().cpu().numpy().view(np.uint32).reshape(-1)
+
+
+def assert_q_equal(g: ops.NVFP4, o: dict, what=""):
+    torch.cuda.synchronize()
+    assert np.array_equal(npu8(g.tensor_amax), o["tensor_amax"]), f"{what}: tensor amax"
+    assert np.array_equal(npu8(g.tensor_scale), o["tensor_scale"]), f"{what}: tensor scale"
+    assert np.array_equal(npu8(g.scales), o["scales"]), f"{what}: scales"
+    gc, oc = npu8(g.codes), o["codes"]
+    if not np.array_equal(gc, oc):
+        bad = np.nonzero(gc != oc)[0]
+        raise AssertionError(f"{what}: {bad.size} code bytes differ, first at byte {bad[0]}: "
+                             f"gpu {gc[bad[0]]:#04x} oracle {oc[bad[0]]:#04x}")
+
+
+def test_native_library_is_loaded():
+    from fp4_quantization_precision_amd import _lib
+    _lib.lib()
+    maps = open("/proc/self/maps").read()
+    assert os.path.realpath(_lib.LIB_PATH) in maps
+
+
+# ----------------------------------------------------------------------------------
+# Tiny NVFP4 round trip: 64x256 fp32
+# ----------------------------------------------------------------------------------
+
+def test_tiny_roundtrip_chain():
+    xr, xt = inputs.tiny_roundtrip()
+    n = xr.numel()
+    hints = torch.zeros(ops.hint_words(n), dtype=torch.int32, device=DEV)
+    qr = ops.quantize(xr.to(DEV), hints_out=hints)
+    qn = ops.quantize(xt.to(DEV))
+    qg = ops.quantize_guided(xt.to(DEV), hints)
+    h2 = ops.extract_hint(qr.codes, n)
+    cnt = ops.code_mismatch(torch.cat([qr.codes.reshape(-1)] * 2), torch.cat(
+        [qn.codes.reshape(-1), qg.codes.reshape(-1)]), 2, n)
+    o_r = oracle.quantize(xr, 1, 64, 256)
+    o_n = oracle.quantize(xt, 1, 64, 256)
+    o_h = oracle.extract_hint(o_r["codes"], n)
+    o_g = oracle.quantize_guided(xt, 1, 64, 256, o_h)
+    assert_q_equal(qr, o_r, "rollout")
+    assert_q_equal(qn, o_n, "trainer nearest")
+    assert_q_equal(qg, o_g, "trainer guided")
+    assert np.array_equal(hints_np(hints), o_h)
+    assert np.array_equal(hints_np(h2), o_h)
+    o_c = oracle.code_mismatch(np.concatenate([o_r["codes"]] * 2),
+                               np.concatenate([o_n["codes"], o_g["codes"]]), 2, n)
+    got = cnt.cpu().numpy().astype(np.uint64)
+    assert np.array_equal(got, o_c)
+    assert got[1, 0] <= got[0, 0]
+    print(f"\ntiny round trip: mismatches nearest {got[0, 0]} -> guided {got[1, 0]} of {n}")
+
+
+# ----------------------------------------------------------------------------------
+# Quantizer edge cases
+# ----------------------------------------------------------------------------------
+
+def _edge_tensor(kind, seed=0):
+    rng = np.random.default_rng(seed)
+    if kind == "all_zero":
+        return np.zeros((2, 16, 64), np.float32)
+    if kind == "neg_zero":
+        x = rng.standard_normal((1, 8, 64)).astype(np.float32)
+        x[0, :4] = -0.0
+        return x
+    if kind == "zero_and_subnormal_blocks":
+        x = rng.standard_normal((3, 32, 96)).astype(np.float32)
+        x[:, :, :16] = 0
+        x[:, 3, 16:48] *= 2.0 ** -13
+        x[:, 5, 48:64] *= 2.0 ** -17
+        x[1, 0, 95] = 3000.0
+        return x
+    if kind == "midpoints":
+        # unit scale (A_T = 2688, block max 6): every E2M1 midpoint and its neighbours
+        mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+        vals = []
+        for m in mids + [0.5, 1, 1.5, 2, 3, 4, 6, 6.5, 7.9]:
+            v = np.float32(m)
+            vals += [v, np.nextafter(v, np.float32(0)), np.nextafter(v, np.float32(10)), -v]
+        per = 15
+        nb = -(-len(vals) // per)
+        x = np.zeros((1, 1, 16 * (nb + 1)), np.float32)
+        for i, v in enumerate(vals):
+            b, j = divmod(i, per)
+            x[0, 0, 16 * b] = 6.0
+            x[0, 0, 16 * b + 1 + j] = v
+        x[0, 0, 16 * nb] = 2688.0
+        return x
+    if kind == "scale_rounds_down":
+        # block max / 6 / s_t just below an E4M3 rounding tie: |y| exceeds 6 slightly
+        x = rng.standard_normal((1, 64, 64)).astype(np.float32) * 0.1
+        x[0, 0, 0] = 2688.0
+        for r in range(1, 64):
+            x[0, r, 0] = np.float32(6 * (1 + 1 / 16 - 1e-4) * (2.0 ** (r % 7)))
+        return x
+    if kind == "huge_and_tiny":
+        x = rng.standard_normal((2, 16, 32)).astype(np.float32)
+        x[0] *= 1e30
+        x[1] *= 1e-28
+        return x
+    if kind == "single_row":
+        return rng.standard_normal((1, 1, 16)).astype(np.float32)
+    if kind == "many_small_tensors":
+        return rng.standard_normal((300, 2, 32)).astype(np.float32) * rng.uniform(
+            0.01, 100, (300, 1, 1)).astype(np.float32)
+    if kind == "odd_block_count":
+        return rng.standard_normal((1, 3, 16)).astype(np.float32)
+    raise KeyError(kind)
+
+
+EDGE = ["all_zero", "neg_zero", "zero_and_subnormal_blocks", "midpoints", "scale_rounds_down",
+        "huge_and_tiny", "single_row", "many_small_tensors", "odd_block_count"]
+
+
+@pytest.mark.parametrize("kind", EDGE)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quantize_edges(kind, dtype):
+    x = torch.from_numpy(_edge_tensor(kind))
+    if dtype == "bf16":
+        x = x.to(torch.bfloat16)
+    B, R, Cc = x.shape
+    n = x.numel()
+    hints = torch.full((ops.hint_words(n),), -1, dtype=torch.int32, device=DEV)
+    g = ops.quantize(x.to(DEV), hints_out=hints)
+    o = oracle.quantize(x, B, R, Cc)
+    assert_q_equal(g, o, kind)
+    assert np.array_equal(hints_np(hints), oracle.extract_hint(o["codes"], n))
+    # guided with a random hint stream
+    rng = np.random.default_rng(1)
+    h = rng.integers(0, 2 ** 32, ops.hint_words(n), dtype=np.uint64).astype(np.uint32)
+    gg = ops.quantize_guided(x.to(DEV), torch.from_numpy(h.view(np.int32)).to(DEV))
+    og = oracle.quantize_guided(x, B, R, Cc, h)
+    assert_q_equal(gg, og, kind + " guided")
+    # dequantization
+    dq = ops.dequantize(g, B, R, Cc)
+    torch.cuda.synchronize()
+    assert np.array_equal(dq.cpu().numpy().reshape(-1).view(np.uint32),
+                          oracle.dequantize(o["codes"], o["scales"], o["tensor_scale"], B, R,
+                                            Cc).view(np.uint32))
+
+
+def test_amax_given_and_tensor_amax():
+    x = torch.from_numpy(_edge_tensor("zero_and_subnormal_blocks")).to(torch.bfloat16)
+    B, R, Cc = x.shape
+    am = ops.tensor_amax(x.to(DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(am.cpu().numpy(), oracle.tensor_amax(x, B, R * Cc))
+    out = ops.new_nvfp4((B,), R, Cc, DEV)
+    out.tensor_amax.copy_(am)
+    g = ops.quantize(x.to(DEV), out=out, amax_given=True)
+    assert_q_equal(g, oracle.quantize(x, B, R, Cc), "amax given")
+
+
+def test_empty_tensors():
+    x = torch.zeros((3, 0, 32), dtype=torch.bfloat16, device=DEV)
+    out = ops.new_nvfp4((3,), 0, 32, DEV)
+    out.tensor_scale.fill_(7.0)
+    out.tensor_amax.fill_(7.0)
+    ops.quantize(x, out=out)
+    torch.cuda.synchronize()
+    assert (out.tensor_scale == 0).all() and (out.tensor_amax == 0).all()
+    q = ops.NVFP4(torch.zeros(0, dtype=torch.uint8, device=DEV),
+                  torch.zeros(0, dtype=torch.uint8, device=DEV),
+                  torch.tensor([0.5, 2.0], device=DEV), torch.zeros(2, device=DEV))
+    t = ops.requant_transpose_sr(q, 2, 0, 32, seed=1)
+    torch.cuda.synchronize()
+    assert t.tensor_scale.cpu().tolist() == [0.5, 2.0]
+
+
+def test_boundary_example_from_trace_page():
+    g = json.load(open(os.path.join(GOLDEN, "rounding_boundary.json")))
+    xr = np.zeros((1, 1, 32), np.float32)
+    xt = np.zeros((1, 1, 32), np.float32)
+    xr[0, 0, 0] = xt[0, 0, 0] = 6.0
+    xr[0, 0, 16] = xt[0, 0, 16] = 2688.0
+    xr[0, 0, 1], xt[0, 0, 1] = g["rollout_value"], g["train_value"]
+    h = torch.zeros(1, dtype=torch.int32, device=DEV)
+    qr = ops.quantize(torch.from_numpy(xr).to(DEV), hints_out=h)
+    qn = ops.quantize(torch.from_numpy(xt).to(DEV))
+    qg = ops.quantize_guided(torch.from_numpy(xt).to(DEV), h)
+    torch.cuda.synchronize()
+    code = lambda q: int(q.codes.cpu()[0, 0, 0] >> 4)
+    assert code(qr) == g["rollout_nearest_code"]
+    assert code(qn) == g["train_nearest_code"]
+    assert code(qg) == g["train_guided_code"]
+
+
+# ----------------------------------------------------------------------------------
+# Hints
+# ----------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n", [1, 2, 31, 32, 33, 64, 1000, 4112, 1 << 20, (1 << 20) + 46])
+def test_extract_hint(n):
+    rng = np.random.default_rng(n)
+    codes = rng.integers(0, 256, (n + 1) // 2 + 16, dtype=np.uint8)
+    words = ops.hint_words(n)
+    h = torch.full((words + 2,), -1, dtype=torch.int32, device=DEV)
+    ops.extract_hint(torch.from_numpy(codes).to(DEV), n, h)
+    torch.cuda.synchronize()
+    got = hints_np(h)
+    assert np.array_equal(got[:words], oracle.extract_hint(codes, n))
+    assert (got[words:] == 0xFFFFFFFF).all()  # nothing written past the hint words
+
+
+# ----------------------------------------------------------------------------------
+# MoE expert weights: 48 layers x 64 experts x [2048 x 768] bf16 (two full layers)
+# ----------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("layer", [0, 24, 47])
+def test_moe_weights_layer_full_size(layer):
+    E, R, Cc, L = 64, 2048, 768, 48
+    xr, xt = inputs.moe_expert_weights_layer(layer, E, R, Cc, device=DEV)
+    n = xr.numel()
+    with_hints = layer >= ops.hint_first_layer(L)
+    hints = torch.zeros(ops.hint_words(n), dtype=torch.int32, device=DEV) if with_hints else None
+    qr = ops.quantize(xr, hints_out=hints)
+    qn = ops.quantize(xt)
+    qg = ops.quantize_guided(xt, hints, out=ops.new_nvfp4((E,), R, Cc, DEV)) if with_hints else qn
+    before = ops.code_mismatch(qr.codes.reshape(-1), qn.codes.reshape(-1), E, R * Cc)
+    after = ops.code_mismatch(qr.codes.reshape(-1), qg.codes.reshape(-1), E, R * Cc)
+    torch.cuda.synchronize()
+    per = R * Cc
+    for e in [0, 17, E - 1]:
+        xr_e, xt_e = xr[e].cpu(), xt[e].cpu()
+        o_r = oracle.quantize(xr_e, 1, R, Cc)
+        o_n = oracle.quantize(xt_e, 1, R, Cc)
+        sl = lambda t, div: npu8(t)[e * per // div:(e + 1) * per // div]
+        assert np.array_equal(sl(qr.codes, 2), o_r["codes"]), f"expert {e} rollout codes"
+        assert np.array_equal(sl(qr.scales, 16), o_r["scales"]), f"expert {e} rollout scales"
+        assert npu8(qr.tensor_scale)[e] == o_r["tensor_scale"][0]
+        assert np.array_equal(sl(qn.codes, 2), o_n["codes"]), f"expert {e} trainer codes"
+        o_cn = oracle.code_mismatch(o_r["codes"], o_n["codes"], 1, per)
+        assert np.array_equal(before.cpu().numpy()[e].astype(np.uint64), o_cn[0])
+        if with_hints:
+            o_h = oracle.extract_hint(o_r["codes"], per)
+            assert np.array_equal(hints_np(hints)[e * per // 32:(e + 1) * per // 32], o_h)
+            o_g = oracle.quantize_guided(xt_e, 1, R, Cc, o_h)
+            assert np.array_equal(sl(qg.codes, 2), o_g["codes"]), f"expert {e} guided codes"
+            assert np.array_equal(sl(qg.scales, 16), o_g["scales"])
+            o_cg = oracle.code_mismatch(o_r["codes"], o_g["codes"], 1, per)
+            assert np.array_equal(after.cpu().numpy()[e].astype(np.uint64), o_cg[0])
+    b, a = before.sum(0).tolist(), after.sum(0).tolist()
+    assert a[0] <= b[0]
+    print(f"\nlayer {layer}: mismatch rate nearest {b[0] / n:.3e} (adjacent {b[1] / max(b[0], 1):.4f})"
+          f" -> {'guided' if with_hints else 'nearest'} {a[0] / n:.3e}")
+
+
+# ----------------------------------------------------------------------------------
+# Activations: 32768 x 4096 bf16, Student-t(4) with 8 outlier channels
+# ----------------------------------------------------------------------------------
+
+def test_activations_full_size():
+    T, H = 32768, 4096
+    xr, xt, _ = inputs.activations(T, H, device=DEV)
+    n = xr.numel()
+    hints = torch.zeros(ops.hint_words(n), dtype=torch.int32, device=DEV)
+    qr = ops.quantize(xr, hints_out=hints)
+    qg = ops.quantize_guided(xt, hints)
+    qn = ops.quantize(xt)
+    cnt = ops.code_mismatch(torch.cat([qr.codes.reshape(-1)] * 2),
+                            torch.cat([qn.codes.reshape(-1), qg.codes.reshape(-1)]), 2, n)
+    torch.cuda.synchronize()
+    xr_c, xt_c = xr.cpu(), xt.cpu()
+    am_r = oracle.tensor_amax(xr_c, 1, n)
+    am_t = oracle.tensor_amax(xt_c, 1, n)
+    assert npu8(qr.tensor_amax)[0] == am_r[0] and npu8(qg.tensor_amax)[0] == am_t[0]
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 1, T - 1], rng.choice(T, 61, replace=False)]))
+    for r in rows:
+        o_r = oracle.quantize(xr_c[r:r + 1], 1, 1, H, amax=am_r)
+        o_h = oracle.extract_hint(o_r["codes"], H)
+        o_g = oracle.quantize_guided(xt_c[r:r + 1], 1, 1, H, o_h, amax=am_t)
+        assert np.array_equal(npu8(qr.codes[r]), o_r["codes"]), f"row {r}"
+        assert np.array_equal(npu8(qr.scales[r]), o_r["scales"]), f"row {r}"
+        assert np.array_equal(hints_np(hints)[r * H // 32:(r + 1) * H // 32], o_h), f"row {r}"
+        assert np.array_equal(npu8(qg.codes[r]), o_g["codes"]), f"row {r} guided"
+        assert np.array_equal(npu8(qg.scales[r]), o_g["scales"]), f"row {r} guided"
+    c = cnt.cpu().numpy()
+    assert c[1, 0] <= c[0, 0]
+    print(f"\nactivations: mismatch rate nearest {c[0, 0] / n:.3e} -> guided {c[1, 0] / n:.3e}")
+
+
+# ----------------------------------------------------------------------------------
+# Transpose-requantize with stochastic rounding
+# ----------------------------------------------------------------------------------
+
+def test_transpose_sr_full_size():
+    N = 8192
+    x = inputs.transpose_source(N, N, device=DEV)
+    q = ops.quantize(x)
+    t0 = ops.requant_transpose_sr(q, 1, N, N, seed=0)
+    torch.cuda.synchronize()
+    xc = x.cpu()
+    o = oracle.quantize(xc, 1, N, N)
+    assert_q_equal(q, o, "8192^2 nearest")
+    ot = oracle.requant_transpose_sr(o["codes"], o["scales"], o["tensor_scale"], 1, N, N, 0)
+    assert np.array_equal(npu8(t0.codes), ot["codes"])
+    assert np.array_equal(npu8(t0.scales), ot["scales"])
+    assert np.array_equal(npu8(t0.tensor_scale), ot["tensor_scale"])
+
+
+SR_SHAPES = [(1, 16, 16), (1, 48, 80), (3, 272, 96), (2, 16, 1040), (1, 32, 64), (2, 528, 144),
+             (1, 256, 64), (1, 1024, 1024)]
+
+
+@pytest.mark.parametrize("shape", SR_SHAPES)
+def test_transpose_sr_shapes(shape):
+    B, R, Cc = shape
+    c, s, ts = inputs.random_nvfp4(B, R, Cc, seed=R + Cc, zero_block_frac=0.05)
+    q = ops.NVFP4(c.to(DEV), s.to(DEV), ts.to(DEV), torch.zeros(B, device=DEV))
+    for seed in [0, 2 ** 40 + 3]:
+        t = ops.requant_transpose_sr(q, B, R, Cc, seed=seed)
+        torch.cuda.synchronize()
+        o = oracle.requant_transpose_sr(c, s, ts, B, R, Cc, seed)
+        assert np.array_equal(npu8(t.codes), o["codes"]), f"{shape} seed {seed}"
+        assert np.array_equal(npu8(t.scales), o["scales"]), f"{shape} seed {seed}"
+        assert np.array_equal(npu8(t.tensor_scale), o["tensor_scale"])
+
+
+def test_transpose_sr_64_seeds_unbiased():
+    """All 64 seeds on a 1024x1024 tensor nearest-quantized from N(0,1): bit-exact
+    against the oracle, and the mean over seeds of the requantized values tracks
+    the exact transposed values up to the 8-bit resolution of the random bytes."""
+    N = 1024
+    x = inputs.transpose_source(N, N, device=DEV)
+    q = ops.quantize(x)
+    torch.cuda.synchronize()
+    o = oracle.quantize(x.cpu(), 1, N, N)
+    assert_q_equal(q, o, "1024^2")
+    u = oracle.dequantize(o["codes"], o["scales"], np.ones(1, np.float32), 1, N, N).reshape(N, N).T
+    acc = np.zeros((N, N))
+    for seed in range(64):
+        t = ops.requant_transpose_sr(q, 1, N, N, seed=seed)
+        torch.cuda.synchronize()
+        ot = oracle.requant_transpose_sr(o["codes"], o["scales"], o["tensor_scale"], 1, N, N, seed)
+        assert np.array_equal(npu8(t.codes), ot["codes"]), f"seed {seed}"
+        assert np.array_equal(npu8(t.scales), ot["scales"]), f"seed {seed}"
+        acc += oracle.dequantize(ot["codes"], ot["scales"], np.ones(1, np.float32), 1, N,
+                                 N).reshape(N, N)
+    mean = acc / 64
+    rel = (mean - u).sum() / np.abs(u).sum()
+    assert abs(rel) < 2e-3, rel
+
+
+# ----------------------------------------------------------------------------------
+# Grouped GEMM
+# ----------------------------------------------------------------------------------
+
+def _gemm_check(counts, n, k, seed=5, sample=None, strict=True):
+    """strict: |gpu - ref| <= 1e-3 * sum|a*w| (holds when |out| << sum|a*w|, as for the
+    full-size random workloads).  Otherwise the bf16 rounding of the output is added:
+    |bf16_rne(v) - v| <= 2^-8 |v|, so |gpu - ref| <= 1e-3 * sum|a*w| + 2^-8 (1 + 2^-7) |ref|
+    (the fp32 accumulation error, below K * 2^-24 * sum|a*w|, fits in the first term)."""
+    G = len(counts)
+    M = int(sum(counts))
+    a, w, off = inputs.grouped_gemm_inputs(groups=G, tokens=M, k=k, n=n, device="cpu", seed=seed,
+                                           counts=counts)
+    ow = oracle.quantize(w, G, n, k)
+    wq = ops.NVFP4(torch.from_numpy(ow["codes"]).to(DEV), torch.from_numpy(ow["scales"]).to(DEV),
+                   torch.from_numpy(ow["tensor_scale"]).to(DEV), torch.zeros(G, device=DEV))
+    out = ops.grouped_gemm_nvfp4(a.to(DEV), off.to(DEV), wq, n, k)
+    torch.cuda.synchronize()
+    if sample is None:
+        rows = np.arange(M)
+    else:
+        rng = np.random.default_rng(seed)
+        o = off.numpy()
+        edges = np.concatenate([o[:-1][np.diff(o) > 0], o[1:][np.diff(o) > 0] - 1])
+        rows = np.unique(np.concatenate([edges, rng.choice(M, sample, replace=False)]))
+    ref, asum = oracle.grouped_gemm(a, off, n, k, ow["codes"], ow["scales"], ow["tensor_scale"],
+                                    rows=rows)
+    got = out.float().cpu().numpy()[rows].astype(np.float64)
+    err = np.abs(got - ref)
+    bound = 1e-3 * asum
+    if not strict:
+        bound = bound + 2.0 ** -8 * (1 + 2.0 ** -7) * np.abs(ref)
+    assert np.all(err <= bound), f"max err/bound {np.max(err / np.maximum(bound, 1e-300))}"
+    rb = torch.from_numpy(ref).to(torch.bfloat16).float().numpy()
+    ulp = np.abs(got - rb) / np.maximum(np.spacing(np.abs(rb).astype(np.float32)) * 65536, 1e-300)
+    return float(np.max(err / np.maximum(bound, 1e-300))), float(np.max(ulp))
+
+
+def test_grouped_gemm_moe_full_size():
+    """32 experts, Zipf(1.1) counts summing to 16384, K = 2048, N = 768."""
+    counts = inputs.zipf_counts(32, 16384, 1.1)
+    r, u = _gemm_check(counts, 768, 2048, sample=96)
+    print(f"\ngrouped GEMM 32x[16384x2048x768]: max err/bound {r:.3e}, max bf16-ulp {u:.1f}")
+
+
+def test_grouped_gemm_forward_shape():
+    """64 experts, Zipf(1.1) counts summing to 16384, K = 768, N = 2048."""
+    counts = inputs.zipf_counts(64, 16384, 1.1)
+    r, u = _gemm_check(counts, 2048, 768, seed=6, sample=64)
+    print(f"\ngrouped GEMM 64x[16384x768x2048]: max err/bound {r:.3e}, max bf16-ulp {u:.1f}")
+
+
+GEMM_EDGES = [
+    ([5, 0, 7, 1], 64, 64), ([1], 2, 16), ([130, 3], 66, 80), ([0, 0, 257], 200, 48),
+    ([128, 128], 128, 128), ([64] * 5, 256, 2064), ([1, 2, 3, 4, 5, 6, 7], 130, 32),
+]
+
+
+@pytest.mark.parametrize("counts,n,k", GEMM_EDGES)
+def test_grouped_gemm_edges(counts, n, k):
+    _gemm_check(counts, n, k, strict=False)
+
+
+def test_grouped_gemm_closed_form():
+    """Small integers times W = 1 (code 2, scale 1.0, tensor scale 0.5): each output is
+    half a row sum, exact in bf16."""
+    G, n, k = 2, 64, 64
+    counts = [3, 5]
+    off = inputs.group_offsets(counts)
+    A = (np.arange(8 * k).reshape(8, k) % 5 - 2).astype(np.float32)
+    a = torch.from_numpy(A).to(torch.bfloat16)
+    wq = ops.NVFP4(torch.full((G * n * k // 2,), 0x22, dtype=torch.uint8, device=DEV),
+                   torch.full((G * n * k // 16,), 0x38, dtype=torch.uint8, device=DEV),
+                   torch.tensor([0.5, 0.5], device=DEV), torch.zeros(G, device=DEV))
+    out = ops.grouped_gemm_nvfp4(a.to(DEV), off.to(DEV), wq, n, k)
+    torch.cuda.synchronize()
+    want = 0.5 * A.sum(axis=1)[:, None] * np.ones((1, n))
+    assert np.array_equal(out.float().cpu().numpy(), want)
+
+
+# ----------------------------------------------------------------------------------
+# Mismatch counting
+# ----------------------------------------------------------------------------------
+
+def test_code_mismatch_random():
+    rng = np.random.default_rng(3)
+    B, per = 5, 4096
+    a = rng.integers(0, 256, B * per // 2, dtype=np.uint8)
+    b = a.copy()
+    flip = rng.random(b.size) < 0.05
+    b[flip] = rng.integers(0, 256, flip.sum(), dtype=np.uint8)
+    got = ops.code_mismatch(torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV), B, per)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy().astype(np.uint64), oracle.code_mismatch(a, b, B, per))
