@@ -1,0 +1,309 @@
+"""Benchmark of the block-scaled FP4 hot path on one MI355X.
+
+One step = the whole path over the MoE expert-weights workload: 48 layers x 64
+experts x [2048 x 768] bf16 weights, a rollout copy X_r and a training copy
+X_t, both resident in HBM.  Per layer:
+
+  1. tensor amax of X_r and X_t (per expert)
+  2. rollout nearest quantize of X_r; for the latter half of the layers the
+     packed 1-bit hint is emitted in the same pass
+  3. trainer nearest quantize of X_t (the unguided baseline)
+  4. trainer guided quantize of X_t with the hints (latter half of the layers)
+  5. code-mismatch counts rollout vs trainer (before / after guidance)
+  6. dequantize -> transpose -> stochastic-rounding requantize of the trainer's
+     weights (the backward copy), Philox seed = layer
+  7. grouped GEMM: 16384 bf16 token rows, Zipf(1.1) over the 64 experts, times
+     the trainer's NVFP4 weights (K = 768, N = 2048), bf16 out
+
+`value` is the step's algorithmic bytes (every input read once, every output
+written once) over the measured step time, in GB/s.  Per-kernel durations
+come from HIP events recorded on the launch stream around each call during the
+timed steps.  The CPU oracle is timed on a bounded sample of the same work.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 2]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+LAYERS, EXPERTS, ROWS, COLS = 48, 64, 2048, 768
+TOKENS = 16384
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--layers", type=int, default=LAYERS)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run one 1 GiB device copy (reference for HBM byte counters)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the path has no "
+                                   "multi-GPU leg (--gpus must be 1)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from fp4_quantization_precision_amd import _lib, inputs, ops
+    from fp4_quantization_precision_amd._lib import TQ_AMAX_GIVEN, TQ_BF16
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = _lib.lib()
+    stream = torch.cuda.current_stream()
+    sp = C.c_void_p(stream.cuda_stream)
+    P = lambda t: C.c_void_p(t.data_ptr()) if t is not None else None
+
+    nl = args.layers
+    first_hint = ops.hint_first_layer(LAYERS)
+    per = ROWS * COLS
+    n_layer = EXPERTS * per
+
+    # ---------------- inputs resident in HBM ----------------
+    t_gen = time.perf_counter()
+    XR = torch.empty((nl, EXPERTS, ROWS, COLS), dtype=torch.bfloat16, device=dev)
+    XT = torch.empty_like(XR)
+    for l in range(nl):
+        xr, xt = inputs.moe_expert_weights_layer(l, EXPERTS, ROWS, COLS, device=dev)
+        XR[l].copy_(xr)
+        XT[l].copy_(xt)
+        del xr, xt
+    counts = inputs.zipf_counts(EXPERTS, TOKENS, 1.1)
+    OFF = inputs.group_offsets(counts).to(dev)
+    gA = torch.Generator(device=dev)
+    gA.manual_seed(5)
+    A = torch.randn((nl, TOKENS, COLS), generator=gA, device=dev).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+
+    # ---------------- outputs ----------------
+    def q_bufs():
+        return ops.NVFP4(torch.empty((nl, EXPERTS, ROWS, COLS // 2), dtype=torch.uint8, device=dev),
+                         torch.empty((nl, EXPERTS, ROWS, COLS // 16), dtype=torch.uint8, device=dev),
+                         torch.empty((nl, EXPERTS), dtype=torch.float32, device=dev),
+                         torch.empty((nl, EXPERTS), dtype=torch.float32, device=dev))
+    QR, QN, QG = q_bufs(), q_bufs(), q_bufs()
+    nh = max(nl - first_hint, 0)
+    H = torch.empty((max(nh, 1), ops.hint_words(n_layer)), dtype=torch.int32, device=dev)
+    CNT = torch.empty((nl, 2, EXPERTS, 2), dtype=torch.int64, device=dev)
+    QT = ops.NVFP4(torch.empty((nl, EXPERTS, COLS, ROWS // 2), dtype=torch.uint8, device=dev),
+                   torch.empty((nl, EXPERTS, COLS, ROWS // 16), dtype=torch.uint8, device=dev),
+                   torch.empty((nl, EXPERTS), dtype=torch.float32, device=dev), None)
+    OUT = torch.empty((nl, TOKENS, ROWS), dtype=torch.bfloat16, device=dev)
+
+    # ---------------- pre-bound calls (validated once by the library) ----------------
+    calls = []  # (category, fn, args)
+    for l in range(nl):
+        hinted = l >= first_hint
+        hl = H[l - first_hint] if hinted else None
+        trainer = QG if hinted else QN
+        calls.append(("amax", L.tq_tensor_amax, (P(XR[l]), TQ_BF16, EXPERTS, per, P(QR.tensor_amax[l]), sp)))
+        calls.append(("quantize_hint" if hinted else "quantize", L.tq_quantize,
+                      (P(XR[l]), TQ_BF16, EXPERTS, ROWS, COLS, P(QR.tensor_amax[l]), P(QR.codes[l]),
+                       P(QR.scales[l]), P(QR.tensor_scale[l]), P(hl), TQ_AMAX_GIVEN, sp)))
+        calls.append(("amax", L.tq_tensor_amax, (P(XT[l]), TQ_BF16, EXPERTS, per, P(QN.tensor_amax[l]), sp)))
+        calls.append(("quantize", L.tq_quantize,
+                      (P(XT[l]), TQ_BF16, EXPERTS, ROWS, COLS, P(QN.tensor_amax[l]), P(QN.codes[l]),
+                       P(QN.scales[l]), P(QN.tensor_scale[l]), None, TQ_AMAX_GIVEN, sp)))
+        if hinted:
+            calls.append(("guided", L.tq_quantize_guided,
+                          (P(XT[l]), TQ_BF16, EXPERTS, ROWS, COLS, P(QN.tensor_amax[l]), P(hl),
+                           P(QG.codes[l]), P(QG.scales[l]), P(QG.tensor_scale[l]), TQ_AMAX_GIVEN, sp)))
+        calls.append(("mismatch", L.tq_code_mismatch,
+                      (P(QR.codes[l]), P(QN.codes[l]), EXPERTS, per, P(CNT[l, 0]), sp)))
+        if hinted:
+            calls.append(("mismatch", L.tq_code_mismatch,
+                          (P(QR.codes[l]), P(QG.codes[l]), EXPERTS, per, P(CNT[l, 1]), sp)))
+        calls.append(("sr_transpose", L.tq_requant_transpose_sr,
+                      (P(trainer.codes[l]), P(trainer.scales[l]), P(trainer.tensor_scale[l]), EXPERTS,
+                       ROWS, COLS, C.c_uint64(l), P(QT.codes[l]), P(QT.scales[l]),
+                       P(QT.tensor_scale[l]), sp)))
+        calls.append(("gemm", L.tq_grouped_gemm_nvfp4,
+                      (P(A[l]), P(OFF), EXPERTS, TOKENS, ROWS, COLS, P(trainer.codes[l]),
+                       P(trainer.scales[l]), P(trainer.tensor_scale[l]), P(OUT[l]), sp)))
+
+    # algorithmic bytes per call (inputs read once + outputs written once)
+    def call_bytes(cat):
+        n = n_layer
+        return {
+            "amax": 2.0 * n,
+            "quantize": n * (2 + 0.5 + 1 / 16),
+            "quantize_hint": n * (2 + 0.5 + 1 / 16 + 1 / 8),
+            "guided": n * (2 + 1 / 8 + 0.5 + 1 / 16),
+            "mismatch": n * (0.5 + 0.5),
+            "sr_transpose": n * 2 * (0.5 + 1 / 16),
+            "gemm": TOKENS * COLS * 2 + n * (0.5 + 1 / 16) + TOKENS * ROWS * 2,
+        }[cat]
+    gemm_flops = 2.0 * TOKENS * COLS * ROWS
+    step_bytes = sum(call_bytes(c) for c, _, _ in calls)
+    step_flops = gemm_flops * nl
+
+    def run_step(events=None):
+        for i, (cat, fn, a) in enumerate(calls):
+            if events is not None:
+                events[i][0].record(stream)
+            st = fn(*a)
+            if st != 0:
+                raise RuntimeError(f"{cat}: {L.tq_status_string(st).decode()}")
+            if events is not None:
+                events[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    # ---------------- timed steps ----------------
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in calls] for _ in range(args.steps)]
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step_ev[s][0].record(stream)
+        run_step(ev[s])
+        step_ev[s][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+    ev_step_ms = float(np.mean([a.elapsed_time(b) for a, b in step_ev]))
+
+    per_cat = {}
+    for s in range(args.steps):
+        for i, (cat, _, _) in enumerate(calls):
+            per_cat.setdefault(cat, []).append(ev[s][i][0].elapsed_time(ev[s][i][1]))
+    kernels = {}
+    for cat, ts in per_cat.items():
+        us = 1e3 * float(np.mean(ts))
+        ent = {"launches_per_step": len(ts) // args.steps, "avg_us": round(us, 2)}
+        if cat == "gemm":
+            ent["TFLOP/s"] = round(gemm_flops / (us * 1e-6) / 1e12, 1)
+            ent["frac_bf16_mfma_peak"] = round(ent["TFLOP/s"] / BF16_MFMA_PEAK_TFLOPS, 4)
+        ent["GB/s"] = round(call_bytes(cat) / (us * 1e-6) / 1e9, 1)
+        ent["frac_hbm_peak"] = round(ent["GB/s"] / HBM_PEAK_GBS, 4)
+        ent["share_of_step"] = round(sum(ts) / args.steps / ev_step_ms, 4)
+        kernels[cat] = ent
+
+    # mismatch statistics of the last step
+    cnt = CNT.sum(dim=2).cpu().numpy()
+    mism = {"nearest_rate": float(cnt[:, 0, 0].sum() / (nl * n_layer)),
+            "nearest_adjacent_frac": float(cnt[:, 0, 1].sum() / max(cnt[:, 0, 0].sum(), 1))}
+    if nh:
+        mism["hinted_layers_nearest_rate"] = float(cnt[first_hint:, 0, 0].sum() / (nh * n_layer))
+        mism["hinted_layers_guided_rate"] = float(cnt[first_hint:, 1, 0].sum() / (nh * n_layer))
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    dom = kernels["quantize"]
+    roofline = {"bound": "hbm", "kernel": "quantize_kernel<bf16,nearest> (tq_quantize, amax given)",
+                "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom["GB/s"] / HBM_PEAK_GBS, 4), "traffic": None,
+                "bytes_per_launch": call_bytes("quantize"), "avg_launch_us": dom["avg_us"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(XR, XT, A, counts, first_hint)
+
+    line = {
+        "metric": "quantize/guided-quantize GB/s and % of HBM peak; grouped-GEMM TFLOP/s",
+        "value": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"moe-expert-weights {nl}x{EXPERTS}x[{ROWS}x{COLS}] bf16 "
+                               f"(rollout+trainer copies; hints for layers >= {first_hint}; "
+                               f"SR transpose; grouped GEMM {TOKENS} tokens/layer)",
+                   "layers": nl, "experts": EXPERTS, "rows": ROWS, "cols": COLS,
+                   "gemm_tokens_per_layer": TOKENS, "gemm_k": COLS, "gemm_n": ROWS,
+                   "parallelism": "single GPU"},
+        "step_bytes": step_bytes,
+        "step_gemm_tflops": round(step_flops / (ms_per_step * 1e-3) / 1e12, 1),
+        "event_ms_per_step": round(ev_step_ms, 3),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "mismatch": mism,
+        "input_generation_s": round(t_gen, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(XR, XT, A, counts, first_hint):
+    """The CPU oracle on a bounded sample of one step: experts 0 and 1 of layer
+    `first_hint` (a hinted layer) through amax, nearest (rollout + trainer),
+    hints, guided, mismatch counts and the SR transpose, plus the grouped-GEMM
+    rows of the same share of the layer's tokens (2/64 of 16384 rows), scaled to
+    GB/s with the same algorithmic bytes as the GPU step."""
+    import numpy as np
+
+    import oracle
+    l, ne = first_hint, 2
+    per = ROWS * COLS
+    xr = XR[l, :ne].cpu()
+    xt = XT[l, :ne].cpu()
+    a = A[l].cpu()
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows = np.arange(0, TOKENS, 32)[: TOKENS * ne // EXPERTS]  # 512 token rows spread over the layer
+    t0 = time.perf_counter()
+    qr = oracle.quantize(xr, ne, ROWS, COLS)
+    h = oracle.extract_hint(qr["codes"], ne * per)
+    qn = oracle.quantize(xt, ne, ROWS, COLS)
+    qg = oracle.quantize_guided(xt, ne, ROWS, COLS, h, amax=qn["tensor_amax"])
+    oracle.code_mismatch(qr["codes"], qn["codes"], ne, per)
+    oracle.code_mismatch(qr["codes"], qg["codes"], ne, per)
+    oracle.requant_transpose_sr(qg["codes"], qg["scales"], qg["tensor_scale"], ne, ROWS, COLS, l)
+    t_q = time.perf_counter() - t0
+    # GEMM rows need every expert's weights: quantize the trainer weights of all
+    # experts with the GPU-independent oracle first (not timed: it is the
+    # quantize step, already sampled above), then time the rows.
+    wq = oracle.quantize(XT[l].cpu(), EXPERTS, ROWS, COLS)
+    t1 = time.perf_counter()
+    oracle.grouped_gemm(a, off, ROWS, COLS, wq["codes"], wq["scales"], wq["tensor_scale"], rows=rows)
+    t_g = time.perf_counter() - t1
+    n = ne * per
+    q_bytes = n * (2.0 * 2 + (2 + 0.5 + 1 / 16 + 1 / 8) + (2 + 0.5 + 1 / 16) + (2 + 1 / 8 + 0.5 + 1 / 16)
+                   + 2 * 1.0 + 2 * (0.5 + 1 / 16))
+    g_bytes = (TOKENS * COLS * 2 + EXPERTS * per * (0.5 + 1 / 16) + TOKENS * ROWS * 2) * rows.size / TOKENS
+    secs = t_q + t_g
+    return {"value": round((q_bytes + g_bytes) / secs / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"layer {l}, experts 0-1 ({n} weights): amax, nearest x2, hints, guided, "
+                      f"mismatch x2, SR transpose ({t_q:.1f} s); grouped-GEMM fp64 rows "
+                      f"{rows.size}/{TOKENS} of the layer ({t_g:.1f} s)",
+            "seconds": round(secs, 2)}
+
+
+if __name__ == "__main__":
+    main()

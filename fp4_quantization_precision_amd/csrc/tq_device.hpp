@@ -122,6 +122,97 @@ __device__ __forceinline__ uint32_t e2m1_code(float y, uint32_t m)
 }
 
 // ---------------------------------------------------------------------------
+// Fast forms used by the kernels.  Each one is an exact re-expression of the
+// rules above (checked bit for bit against the CPU oracle by the GPU tests).
+// ---------------------------------------------------------------------------
+
+// Eight nearest codes packed into one dword (element i in nibble i).  gfx950's
+// v_cvt_scalef32_pk_fp4_f32 with scale 1 rounds to nearest even and saturates at
+// 6 exactly like e2m1_nearest/e2m1_code for every finite binary32 input, except
+// that it keeps the sign of a value that rounds to zero; the mask below turns
+// every -0 nibble (code 8) into +0.
+__device__ __forceinline__ uint32_t clear_negative_zero(uint32_t w)
+{
+    const uint32_t mag = w & 0x77777777u;
+    const uint32_t nonzero = (mag + 0x77777777u) & 0x88888888u;  // bit 3 set iff magnitude != 0
+    return mag | (w & nonzero);
+}
+
+__device__ __forceinline__ uint32_t pack8_nearest(const float y[8])
+{
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], 1.0f, 3);
+    return clear_negative_zero(w);
+}
+
+// Mantissa bits (m & 1) of eight packed codes, gathered into bits 0..7.
+__device__ __forceinline__ uint32_t parity8(uint32_t w)
+{
+    uint32_t x = w & 0x11111111u;
+    x = (x | (x >> 3)) & 0x03030303u;
+    x = (x | (x >> 6)) & 0x000F000Fu;
+    x = (x | (x >> 12)) & 0x000000FFu;
+    return x;
+}
+
+typedef float tq_f32x2 __attribute__((ext_vector_type(2)));
+
+// The two signed E2M1 values of byte `sel` (0..3) of w (low nibble first):
+// v_cvt_scalef32_pk_f32_fp4 with scale 1 is exact for all 256 byte values.
+template <int SEL>
+__device__ __forceinline__ tq_f32x2 fp4x2_to_f32(uint32_t w)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+
+// High halves of two binary32 values as one dword (lo from a, hi from b).  Used
+// for values whose low 16 bits are zero (exact bf16).
+__device__ __forceinline__ uint32_t pack_hi16(float a, float b)
+{
+    return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+
+// Floor grid index of a >= 0 from its bits: above 1 the grid is a binary float
+// with one mantissa bit, so lo = (bits >> 22) - 252 (the exponent and the top
+// mantissa bit); [0.5, 1) gives 1 and [0, 0.5) gives 0; clamped to 7.
+__device__ __forceinline__ uint32_t e2m1_floor_bits(float a)
+{
+    const int b = (int)(__float_as_uint(a) >> 22) - 252;
+    const int lo = b > (int)(a >= 0.5f) ? b : (int)(a >= 0.5f);
+    return (uint32_t)(lo < 7 ? lo : 7);
+}
+
+// e2m1_guided without compare chains: a is on the grid iff the bits below the
+// grid's resolution are zero (22 mantissa bits above 1, 23 in [0.5, 1), all of
+// them below 0.5).  Off the grid the bracket is (lo, lo+1) and the hint picks
+// the end with its parity: lo + ((lo ^ h) & 1).  a >= 6 gives 7.
+__device__ __forceinline__ uint32_t e2m1_guided_bits(float a, uint32_t h)
+{
+    const uint32_t bits = __float_as_uint(a);
+    const uint32_t lo = e2m1_floor_bits(a);
+    const uint32_t mask = a >= 1.0f ? 0x3FFFFFu : (a >= 0.5f ? 0x7FFFFFu : 0x7FFFFFFFu);
+    const bool on_grid = (bits & mask) == 0u;
+    const uint32_t m = on_grid ? lo : lo + ((lo ^ h) & 1u);
+    return m < 7u ? m : 7u;
+}
+
+// e2m1_sr without compare chains: up iff k < 256 (a - G[lo]) / D with
+// D = G[lo+1] - G[lo], i.e. iff G[lo] + k * (D / 256) < a, where G[lo] (at most
+// two significant bits) plus k * D / 256 (at most eight) is exact in binary32.
+// D / 256 is 2^-9 below 2, 2^-8 in [2, 4) and 2^-7 from 4; a >= 6 gives 7.
+__device__ __forceinline__ uint32_t e2m1_sr_bits(float a, float k)
+{
+    const uint32_t lo = e2m1_floor_bits(a);
+    const float glo = lo >= 2u ? __uint_as_float((lo + 252u) << 22) : (lo == 1u ? 0.5f : 0.0f);
+    const float q = lo < 4u ? 0x1p-9f : (lo < 6u ? 0x1p-8f : 0x1p-7f);
+    const uint32_t m = lo + ((glo + k * q < a) ? 1u : 0u);
+    return m < 7u ? m : 7u;
+}
+
+// ---------------------------------------------------------------------------
 // bf16 helpers
 // ---------------------------------------------------------------------------
 

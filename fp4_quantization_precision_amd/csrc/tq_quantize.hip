@@ -17,6 +17,16 @@ namespace tq {
 
 constexpr int kThreads = 256;
 
+// Workgroups per launch of the streaming kernels (spread over the batch).  On
+// MI355X a plain grid-stride stream with one 16-byte access per lane per
+// iteration and one to two thousand workgroups reaches the best HBM rates.
+#ifndef TQ_AMAX_GROUPS
+#define TQ_AMAX_GROUPS 2048
+#endif
+#ifndef TQ_QUANT_GROUPS
+#define TQ_QUANT_GROUPS 2048
+#endif
+
 // ---------------------------------------------------------------------------
 // small fills (used instead of memset nodes, which misbehave under graph replay)
 // ---------------------------------------------------------------------------
@@ -82,17 +92,8 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict_
     for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
         const uint4* xb = x + b * vec_per_tensor;
         uint32_t m = 0;
-        int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-        const int64_t stride = (int64_t)gridDim.x * kThreads;
-        for (; i + 3 * stride < vec_per_tensor; i += 4 * stride) {
-            uint4 q0 = xb[i], q1 = xb[i + stride], q2 = xb[i + 2 * stride],
-                  q3 = xb[i + 3 * stride];
-            m = abs_bits_max(q0, BF16, m);
-            m = abs_bits_max(q1, BF16, m);
-            m = abs_bits_max(q2, BF16, m);
-            m = abs_bits_max(q3, BF16, m);
-        }
-        for (; i < vec_per_tensor; i += stride)
+        for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < vec_per_tensor;
+             i += (int64_t)gridDim.x * kThreads)
             m = abs_bits_max(xb[i], BF16, m);
         m = wave_max_u32(m);
         const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -131,7 +132,7 @@ void launch_amax(const void* x, bool bf16, int64_t batch, int64_t per_tensor, fl
     const int64_t vec = per_tensor * (bf16 ? 2 : 4) / 16;
     if (vec == 0)
         return;
-    dim3 grid(groups_per_tensor(vec / 4, batch, 4096), grid_y(batch));
+    dim3 grid(groups_per_tensor(vec, batch, TQ_AMAX_GROUPS), grid_y(batch));
     if (bf16)
         hipLaunchKernelGGL(amax_kernel<true>, grid, dim3(kThreads), 0, s,
                            static_cast<const uint4*>(x), vec, batch, amax);
@@ -173,7 +174,8 @@ __device__ __forceinline__ void load_block(const void* __restrict__ x, int64_t b
 
 // One lane quantizes one 16-element block: amax -> E4M3 scale -> reciprocal ->
 // 16 codes, packed 8 bytes; MODE_NEAREST_HINT also emits the 16 parity bits and
-// MODE_GUIDED consumes them.
+// MODE_GUIDED consumes them.  Nearest codes come from gfx950's packed FP4
+// conversion (see pack8_nearest), guided codes from the bit-level bracket rule.
 template <bool BF16, int MODE>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(
     const void* __restrict__ x, int64_t blocks_per_tensor, int64_t batch,
@@ -202,30 +204,31 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
             if (s_t != 0.0f)
                 e = e4m3_encode((A_b / 6.0f) / s_t);
             const float dec = e4m3_decode(e);
-            uint32_t lo = 0, hi = 0, par = 0;
+            uint32_t lo = 0, hi = 0;
             if (dec != 0.0f) {
                 const float r_b = 1.0f / (dec * s_t);
+                float y[16];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float y = v[i] * r_b;
-                    const float a = fabsf(y);
-                    uint32_t m;
-                    if (MODE == MODE_GUIDED)
-                        m = e2m1_guided(a, (hin >> i) & 1u);
-                    else
-                        m = e2m1_nearest(a);
-                    const uint32_t c = e2m1_code(y, m);
-                    if (i < 8)
-                        lo |= c << (4 * i);
-                    else
-                        hi |= c << (4 * (i - 8));
-                    par |= (m & 1u) << i;
+                for (int i = 0; i < 16; ++i)
+                    y[i] = v[i] * r_b;
+                if (MODE == MODE_GUIDED) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const uint32_t c = e2m1_code(y[i], e2m1_guided_bits(fabsf(y[i]), (hin >> i) & 1u));
+                        if (i < 8)
+                            lo |= c << (4 * i);
+                        else
+                            hi |= c << (4 * (i - 8));
+                    }
+                } else {
+                    lo = pack8_nearest(y);
+                    hi = pack8_nearest(y + 8);
                 }
             }
             codes[blk] = make_uint2(lo, hi);
             scales[blk] = (uint8_t)e;
             if (MODE == MODE_NEAREST_HINT) {
-                hints[blk] = (uint16_t)par;
+                hints[blk] = (uint16_t)(parity8(lo) | (parity8(hi) << 8));
                 if ((total_blocks & 1) && blk == total_blocks - 1)
                     hints[blk + 1] = 0;  // zero the unused half of the last word
             }
@@ -239,7 +242,7 @@ void launch_quantize(const void* x, bool bf16, int64_t batch, int64_t rows, int6
 {
     const int64_t bpt = rows * cols / 16;
     const int64_t total = bpt * batch;
-    dim3 grid(groups_per_tensor(bpt, batch, 4096), grid_y(batch));
+    dim3 grid(groups_per_tensor(bpt, batch, TQ_QUANT_GROUPS), grid_y(batch));
     uint2* c2 = reinterpret_cast<uint2*>(codes);
     uint16_t* h = reinterpret_cast<uint16_t*>(hints);
 #define TQ_QLAUNCH(B, M)                                                                     \
@@ -387,13 +390,20 @@ __device__ __forceinline__ int signed_pos(uint32_t c)
     return (c & 8u) ? -m : m;
 }
 
+// Mismatches of eight packed codes: a nibble differs iff any of its bits does
+// (OR-folded onto the nibble's low bit, then counted); adjacency is checked only
+// for the differing nibbles.
 __device__ __forceinline__ void count_word(uint32_t a, uint32_t b, uint32_t& mism, uint32_t& adj)
 {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t ca = (a >> (4 * i)) & 15u, cb = (b >> (4 * i)) & 15u;
-        const int d = signed_pos(ca) - signed_pos(cb);
-        mism += (ca != cb) ? 1u : 0u;
+    uint32_t f = a ^ b;
+    f |= f >> 1;
+    f |= f >> 2;
+    f &= 0x11111111u;
+    mism += (uint32_t)__popc(f);
+    while (f) {
+        const int sh = __ffs(f) - 1;  // 4 * nibble index
+        f &= f - 1u;
+        const int d = signed_pos((a >> sh) & 15u) - signed_pos((b >> sh) & 15u);
         adj += (d == 1 || d == -1) ? 1u : 0u;
     }
 }
@@ -409,6 +419,8 @@ __global__ __launch_bounds__(kThreads) void mismatch_kernel(const uint4* __restr
         for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < vec_per_tensor;
              i += (int64_t)gridDim.x * kThreads) {
             const uint4 qa = a[t * vec_per_tensor + i], qb = b[t * vec_per_tensor + i];
+            if (((qa.x ^ qb.x) | (qa.y ^ qb.y) | (qa.z ^ qb.z) | (qa.w ^ qb.w)) == 0u)
+                continue;
             count_word(qa.x, qb.x, mism, adj);
             count_word(qa.y, qb.y, mism, adj);
             count_word(qa.z, qb.z, mism, adj);

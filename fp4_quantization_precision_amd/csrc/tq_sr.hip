@@ -31,13 +31,6 @@ constexpr int kSThreads = 256;
 // so that lanes reading 16-byte runs of consecutive rows hit distinct banks.
 constexpr int kLdsStride = kTR / 2 + 4;
 
-// u = +-G[m] * dec(e) as bf16 bits (exact: at most 6 significant bits).
-__device__ __forceinline__ uint32_t dequant_bf16(uint32_t code, float d)
-{
-    const float mag = e2m1_value(code & 7u) * d;
-    return (__float_as_uint(mag) >> 16) | ((code & 8u) ? 0x8000u : 0u);
-}
-
 __global__ __launch_bounds__(kSThreads) void requant_transpose_sr_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const float* __restrict__ tensor_scale, int64_t batch, int64_t rows, int64_t cols,
@@ -80,11 +73,25 @@ __global__ __launch_bounds__(kSThreads) void requant_transpose_sr_kernel(
                         }
                     }
                 }
+                // u = +-G[m] * dec(e), exact; the two rows' values of column cl+i share one dword
+                uint32_t* dst = u_s + cl * kLdsStride + p;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const uint32_t c0i = ((i < 8 ? q[0].x : q[0].y) >> (4 * (i & 7))) & 15u;
-                    const uint32_t c1i = ((i < 8 ? q[1].x : q[1].y) >> (4 * (i & 7))) & 15u;
-                    u_s[(cl + i) * kLdsStride + p] = dequant_bf16(c0i, d[0]) | (dequant_bf16(c1i, d[1]) << 16);
+                for (int half8 = 0; half8 < 2; ++half8) {
+                    const uint32_t w0 = half8 ? q[0].y : q[0].x;
+                    const uint32_t w1 = half8 ? q[1].y : q[1].x;
+                    tq_f32x2 a0[4], a1[4];
+                    a0[0] = fp4x2_to_f32<0>(w0); a0[1] = fp4x2_to_f32<1>(w0);
+                    a0[2] = fp4x2_to_f32<2>(w0); a0[3] = fp4x2_to_f32<3>(w0);
+                    a1[0] = fp4x2_to_f32<0>(w1); a1[1] = fp4x2_to_f32<1>(w1);
+                    a1[2] = fp4x2_to_f32<2>(w1); a1[3] = fp4x2_to_f32<3>(w1);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                        for (int t = 0; t < 2; ++t) {
+                            const int i = 8 * half8 + 2 * j + t;
+                            dst[i * kLdsStride] = pack_hi16(a0[j][t] * d[0], a1[j][t] * d[1]);
+                        }
+                    }
                 }
             }
         }
@@ -133,9 +140,8 @@ __global__ __launch_bounds__(kSThreads) void requant_transpose_sr_kernel(
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const float y = u[i] * rr;
-                        const uint32_t k = (rw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-                        const uint32_t m = e2m1_sr(fabsf(y), k);
-                        const uint32_t c = e2m1_code(y, m);
+                        const float k = (float)((rw[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+                        const uint32_t c = e2m1_code(y, e2m1_sr_bits(fabsf(y), k));
                         if (i < 8)
                             lo |= c << (4 * i);
                         else
