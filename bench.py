@@ -214,16 +214,29 @@ def main():
         mism["hinted_layers_guided_rate"] = float(cnt[first_hint:, 1, 0].sum() / (nh * n_layer))
 
     if args.copy_calibration:
+        # one plain device copy of 1 GiB (read 1 GiB, write 1 GiB): the yardstick
+        # for the HBM byte counters (FETCH_SIZE / WRITE_SIZE) of the kernels above
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
 
-    dom = kernels["quantize"]
-    roofline = {"bound": "hbm", "kernel": "quantize_kernel<bf16,nearest> (tq_quantize, amax given)",
-                "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(dom["GB/s"] / HBM_PEAK_GBS, 4), "traffic": None,
-                "bytes_per_launch": call_bytes("quantize"), "avg_launch_us": dom["avg_us"]}
+    # the roofline is reported for the kernel with the largest share of the step
+    dom_cat = max(kernels, key=lambda c: kernels[c]["share_of_step"])
+    dom = kernels[dom_cat]
+    kname, ksrc = KERNEL_OF[dom_cat]
+    if dom_cat == "gemm":
+        roofline = {"bound": "mfma", "achieved": dom["TFLOP/s"], "peak": BF16_MFMA_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": dom["frac_bf16_mfma_peak"]}
+    else:
+        roofline = {"bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": dom["frac_hbm_peak"]}
+    roofline.update({"traffic": measured_traffic(dom_cat), "kernel": kname, "category": dom_cat,
+                     "algorithmic_bytes_per_launch": call_bytes(dom_cat),
+                     "avg_launch_us": dom["avg_us"], "share_of_step": dom["share_of_step"]})
+    if dom_cat == "gemm":
+        roofline["algorithmic_flops_per_launch"] = gemm_flops
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -260,6 +273,36 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+# kernel name and source file of each timed category
+KERNEL_OF = {
+    "amax": ("tq::amax_kernel<true>", "tq_quantize.hip"),
+    "quantize": ("tq::quantize_kernel<true, 0>", "tq_quantize.hip"),
+    "quantize_hint": ("tq::quantize_kernel<true, 1>", "tq_quantize.hip"),
+    "guided": ("tq::quantize_kernel<true, 2>", "tq_quantize.hip"),
+    "mismatch": ("tq::mismatch_kernel", "tq_quantize.hip"),
+    "sr_transpose": ("tq::requant_transpose_sr_kernel", "tq_sr.hip"),
+    "gemm": ("tq::grouped_gemm_nvfp4_kernel", "tq_gemm.hip"),
+}
+
+# HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE passes over this
+# benchmark (KiB per dispatch, scaled by what the same counters read for the
+# 1 GiB device copy of --copy-calibration), keyed by the SHA-256 of the kernel's
+# source file when the counters were taken: a changed source reports null.
+TRAFFIC = {
+}
+
+
+def measured_traffic(cat):
+    import hashlib
+    ent = TRAFFIC.get(cat)
+    if ent is None:
+        return None
+    src = os.path.join(ROOT, "fp4_quantization_precision_amd", "csrc", KERNEL_OF[cat][1])
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    return ent["bytes"] if digest == ent["source_sha256"] else None
+
+
 def cpu_baseline(XR, XT, A, counts, first_hint):
     """The CPU oracle on a bounded sample of one step: experts 0 and 1 of layer
     `first_hint` (a hinted layer) through amax, nearest (rollout + trainer),
@@ -275,7 +318,7 @@ def cpu_baseline(XR, XT, A, counts, first_hint):
     xt = XT[l, :ne].cpu()
     a = A[l].cpu()
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-    rows = np.arange(0, TOKENS, 32)[: TOKENS * ne // EXPERTS]  # 512 token rows spread over the layer
+    rows = np.arange(0, TOKENS, 16)[: 2 * TOKENS * ne // EXPERTS]  # 1024 token rows spread over the layer
     t0 = time.perf_counter()
     qr = oracle.quantize(xr, ne, ROWS, COLS)
     h = oracle.extract_hint(qr["codes"], ne * per)

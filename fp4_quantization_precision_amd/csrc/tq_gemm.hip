@@ -62,7 +62,7 @@ struct TileRegs {
     float d[2];   // their two block scales
 };
 
-__global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
+__global__ __launch_bounds__(kGThreads, 3) void grouped_gemm_nvfp4_kernel(
     const uint16_t* __restrict__ a, const int32_t* __restrict__ group_offsets, int num_groups,
     int64_t n, int64_t k, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales,
     const float* __restrict__ w_tensor_scale, uint16_t* __restrict__ out, int n_tiles)
