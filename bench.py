@@ -2,12 +2,13 @@
 
 One step = the whole path over the MoE expert-weights workload: 48 layers x 64
 experts x [2048 x 768] bf16 weights, a rollout copy X_r and a training copy
-X_t, both resident in HBM.  Per layer:
+X_t, both resident in HBM.  The step runs in phases, each one kernel over all
+48 layers:
 
-  1. tensor amax of X_r and X_t (per expert)
+  1. tensor amax of X_r (per expert)
   2. rollout nearest quantize of X_r; for the latter half of the layers the
      packed 1-bit hint is emitted in the same pass
-  3. trainer nearest quantize of X_t (the unguided baseline)
+  3. tensor amax of X_t, trainer nearest quantize of X_t (unguided baseline)
   4. trainer guided quantize of X_t with the hints (latter half of the layers)
   5. code-mismatch counts rollout vs trainer (before / after guidance)
   6. dequantize -> transpose -> stochastic-rounding requantize of the trainer's
@@ -17,8 +18,9 @@ X_t, both resident in HBM.  Per layer:
 
 `value` is the step's algorithmic bytes (every input read once, every output
 written once) over the measured step time, in GB/s.  Per-kernel durations
-come from HIP events recorded on the launch stream around each call during the
-timed steps.  The CPU oracle is timed on a bounded sample of the same work.
+come from HIP events recorded on the launch stream around each phase of the
+timed steps (phase time / launches).  The CPU oracle is timed on a bounded
+sample of the same work.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 2]
 """
@@ -113,35 +115,56 @@ def main():
     OUT = torch.empty((nl, TOKENS, ROWS), dtype=torch.bfloat16, device=dev)
 
     # ---------------- pre-bound calls (validated once by the library) ----------------
-    calls = []  # (category, fn, args)
+    # The step runs as phases, each one kernel over all layers: the rollout's
+    # amax and quantize (with hints for the latter half), the trainer's amax,
+    # nearest and guided quantize, the mismatch counts, the SR transpose and the
+    # grouped GEMM.  Events bracket each phase (one kernel, back to back), so the
+    # per-kernel averages carry no per-call event overhead.
+    phases = {}  # phase name -> list of (category, fn, args)
+
+    def add(phase, cat, fn, a):
+        phases.setdefault(phase, []).append((cat, fn, a))
+
     for l in range(nl):
         hinted = l >= first_hint
         hl = H[l - first_hint] if hinted else None
-        trainer = QG if hinted else QN
-        calls.append(("amax", L.tq_tensor_amax, (P(XR[l]), TQ_BF16, EXPERTS, per, P(QR.tensor_amax[l]), sp)))
-        calls.append(("quantize_hint" if hinted else "quantize", L.tq_quantize,
-                      (P(XR[l]), TQ_BF16, EXPERTS, ROWS, COLS, P(QR.tensor_amax[l]), P(QR.codes[l]),
-                       P(QR.scales[l]), P(QR.tensor_scale[l]), P(hl), TQ_AMAX_GIVEN, sp)))
-        calls.append(("amax", L.tq_tensor_amax, (P(XT[l]), TQ_BF16, EXPERTS, per, P(QN.tensor_amax[l]), sp)))
-        calls.append(("quantize", L.tq_quantize,
-                      (P(XT[l]), TQ_BF16, EXPERTS, ROWS, COLS, P(QN.tensor_amax[l]), P(QN.codes[l]),
-                       P(QN.scales[l]), P(QN.tensor_scale[l]), None, TQ_AMAX_GIVEN, sp)))
-        if hinted:
-            calls.append(("guided", L.tq_quantize_guided,
-                          (P(XT[l]), TQ_BF16, EXPERTS, ROWS, COLS, P(QN.tensor_amax[l]), P(hl),
-                           P(QG.codes[l]), P(QG.scales[l]), P(QG.tensor_scale[l]), TQ_AMAX_GIVEN, sp)))
-        calls.append(("mismatch", L.tq_code_mismatch,
-                      (P(QR.codes[l]), P(QN.codes[l]), EXPERTS, per, P(CNT[l, 0]), sp)))
-        if hinted:
-            calls.append(("mismatch", L.tq_code_mismatch,
-                          (P(QR.codes[l]), P(QG.codes[l]), EXPERTS, per, P(CNT[l, 1]), sp)))
-        calls.append(("sr_transpose", L.tq_requant_transpose_sr,
-                      (P(trainer.codes[l]), P(trainer.scales[l]), P(trainer.tensor_scale[l]), EXPERTS,
-                       ROWS, COLS, C.c_uint64(l), P(QT.codes[l]), P(QT.scales[l]),
-                       P(QT.tensor_scale[l]), sp)))
-        calls.append(("gemm", L.tq_grouped_gemm_nvfp4,
-                      (P(A[l]), P(OFF), EXPERTS, TOKENS, ROWS, COLS, P(trainer.codes[l]),
-                       P(trainer.scales[l]), P(trainer.tensor_scale[l]), P(OUT[l]), sp)))
+        add("amax_rollout", "amax", L.tq_tensor_amax,
+            (P(XR[l]), TQ_BF16, EXPERTS, per, P(QR.tensor_amax[l]), sp))
+    for l in range(nl):
+        hinted = l >= first_hint
+        hl = H[l - first_hint] if hinted else None
+        add("quantize_hint_rollout" if hinted else "quantize_rollout",
+            "quantize_hint" if hinted else "quantize", L.tq_quantize,
+            (P(XR[l]), TQ_BF16, EXPERTS, ROWS, COLS, P(QR.tensor_amax[l]), P(QR.codes[l]),
+             P(QR.scales[l]), P(QR.tensor_scale[l]), P(hl), TQ_AMAX_GIVEN, sp))
+    for l in range(nl):
+        add("amax_trainer", "amax", L.tq_tensor_amax,
+            (P(XT[l]), TQ_BF16, EXPERTS, per, P(QN.tensor_amax[l]), sp))
+    for l in range(nl):
+        add("quantize_trainer", "quantize", L.tq_quantize,
+            (P(XT[l]), TQ_BF16, EXPERTS, ROWS, COLS, P(QN.tensor_amax[l]), P(QN.codes[l]),
+             P(QN.scales[l]), P(QN.tensor_scale[l]), None, TQ_AMAX_GIVEN, sp))
+    for l in range(first_hint, nl):
+        add("guided_trainer", "guided", L.tq_quantize_guided,
+            (P(XT[l]), TQ_BF16, EXPERTS, ROWS, COLS, P(QN.tensor_amax[l]), P(H[l - first_hint]),
+             P(QG.codes[l]), P(QG.scales[l]), P(QG.tensor_scale[l]), TQ_AMAX_GIVEN, sp))
+    for l in range(nl):
+        add("mismatch", "mismatch", L.tq_code_mismatch,
+            (P(QR.codes[l]), P(QN.codes[l]), EXPERTS, per, P(CNT[l, 0]), sp))
+        if l >= first_hint:
+            add("mismatch", "mismatch", L.tq_code_mismatch,
+                (P(QR.codes[l]), P(QG.codes[l]), EXPERTS, per, P(CNT[l, 1]), sp))
+    for l in range(nl):
+        trainer = QG if l >= first_hint else QN
+        add("sr_transpose", "sr_transpose", L.tq_requant_transpose_sr,
+            (P(trainer.codes[l]), P(trainer.scales[l]), P(trainer.tensor_scale[l]), EXPERTS,
+             ROWS, COLS, C.c_uint64(l), P(QT.codes[l]), P(QT.scales[l]), P(QT.tensor_scale[l]), sp))
+    for l in range(nl):
+        trainer = QG if l >= first_hint else QN
+        add("gemm", "gemm", L.tq_grouped_gemm_nvfp4,
+            (P(A[l]), P(OFF), EXPERTS, TOKENS, ROWS, COLS, P(trainer.codes[l]),
+             P(trainer.scales[l]), P(trainer.tensor_scale[l]), P(OUT[l]), sp))
+    calls = [c for ph in phases.values() for c in ph]
 
     # algorithmic bytes per call (inputs read once + outputs written once)
     def call_bytes(cat):
@@ -160,24 +183,24 @@ def main():
     step_flops = gemm_flops * nl
 
     def run_step(events=None):
-        for i, (cat, fn, a) in enumerate(calls):
+        for name, ph in phases.items():
             if events is not None:
-                events[i][0].record(stream)
-            st = fn(*a)
-            if st != 0:
-                raise RuntimeError(f"{cat}: {L.tq_status_string(st).decode()}")
+                events[name][0].record(stream)
+            for cat, fn, a in ph:
+                st = fn(*a)
+                if st != 0:
+                    raise RuntimeError(f"{cat}: {L.tq_status_string(st).decode()}")
             if events is not None:
-                events[i][1].record(stream)
+                events[name][1].record(stream)
 
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
 
     # ---------------- timed steps ----------------
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in calls] for _ in range(args.steps)]
-    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
+    new_ev = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    ev = [{name: new_ev() for name in phases} for _ in range(args.steps)]
+    step_ev = [new_ev() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -189,20 +212,23 @@ def main():
     ms_per_step = 1e3 * wall / args.steps
     ev_step_ms = float(np.mean([a.elapsed_time(b) for a, b in step_ev]))
 
-    per_cat = {}
+    # per category: phase time summed over the timed steps / launches
+    cat_ms, cat_n = {}, {}
     for s in range(args.steps):
-        for i, (cat, _, _) in enumerate(calls):
-            per_cat.setdefault(cat, []).append(ev[s][i][0].elapsed_time(ev[s][i][1]))
+        for name, ph in phases.items():
+            cat = ph[0][0]
+            cat_ms[cat] = cat_ms.get(cat, 0.0) + ev[s][name][0].elapsed_time(ev[s][name][1])
+            cat_n[cat] = cat_n.get(cat, 0) + len(ph)
     kernels = {}
-    for cat, ts in per_cat.items():
-        us = 1e3 * float(np.mean(ts))
-        ent = {"launches_per_step": len(ts) // args.steps, "avg_us": round(us, 2)}
+    for cat in cat_ms:
+        us = 1e3 * cat_ms[cat] / cat_n[cat]
+        ent = {"launches_per_step": cat_n[cat] // args.steps, "avg_us": round(us, 2)}
         if cat == "gemm":
             ent["TFLOP/s"] = round(gemm_flops / (us * 1e-6) / 1e12, 1)
             ent["frac_bf16_mfma_peak"] = round(ent["TFLOP/s"] / BF16_MFMA_PEAK_TFLOPS, 4)
         ent["GB/s"] = round(call_bytes(cat) / (us * 1e-6) / 1e9, 1)
         ent["frac_hbm_peak"] = round(ent["GB/s"] / HBM_PEAK_GBS, 4)
-        ent["share_of_step"] = round(sum(ts) / args.steps / ev_step_ms, 4)
+        ent["share_of_step"] = round(cat_ms[cat] / args.steps / ev_step_ms, 4)
         kernels[cat] = ent
 
     # mismatch statistics of the last step

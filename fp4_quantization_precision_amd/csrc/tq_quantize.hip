@@ -23,6 +23,25 @@ constexpr int kThreads = 256;
 #ifndef TQ_AMAX_GROUPS
 #define TQ_AMAX_GROUPS 2048
 #endif
+#ifndef TQ_STREAM_NT
+#define TQ_STREAM_NT 0
+#endif
+#ifndef TQ_AMAX_UNROLL
+#define TQ_AMAX_UNROLL 4
+#endif
+constexpr int kAmaxUnroll = TQ_AMAX_UNROLL;
+
+// 16-byte load of data read exactly once (nontemporal: no reuse expected in cache)
+__device__ __forceinline__ uint4 stream_load16(const uint4* p)
+{
+#if TQ_STREAM_NT
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
+    return make_uint4(v[0], v[1], v[2], v[3]);
+#else
+    return *p;
+#endif
+}
 #ifndef TQ_QUANT_GROUPS
 #define TQ_QUANT_GROUPS 2048
 #endif
@@ -92,8 +111,19 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict_
     for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
         const uint4* xb = x + b * vec_per_tensor;
         uint32_t m = 0;
-        for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < vec_per_tensor;
-             i += (int64_t)gridDim.x * kThreads)
+        const int64_t stride = (int64_t)gridDim.x * kThreads;
+        int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+        // kAmaxUnroll independent 16-byte loads in flight per lane
+        for (; i + (kAmaxUnroll - 1) * stride < vec_per_tensor; i += kAmaxUnroll * stride) {
+            uint4 q[kAmaxUnroll];
+#pragma unroll
+            for (int u = 0; u < kAmaxUnroll; ++u)
+                q[u] = stream_load16(xb + i + u * stride);
+#pragma unroll
+            for (int u = 0; u < kAmaxUnroll; ++u)
+                m = abs_bits_max(q[u], BF16, m);
+        }
+        for (; i < vec_per_tensor; i += stride)
             m = abs_bits_max(xb[i], BF16, m);
         m = wave_max_u32(m);
         const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;

@@ -6,16 +6,27 @@
 // stochastic rounding.  Arithmetic and random-byte layout are those of
 // include/tq.h.
 //
-// One workgroup owns a tile of kTR input rows x kTC input columns.  Each thread
-// loads two input rows of one 32-column half of the tile (codes + block scales),
-// dequantizes them exactly (u = +-G[m] * dec(e) has at most 6 significant bits,
-// so bf16 holds it) and writes them transposed into LDS, so every output row of
-// the tile is contiguous there.  Then each lane owns one output row and four new
-// 16-element blocks: block amax, E4M3 scale, one Philox4x32-10 call for the
-// block's 16 random bytes, 16 stochastic roundings and one packed store.  A
-// wave's 64 lanes cover 64 output rows, and the four waves of a workgroup cover
-// 4 x 64 = 256 consecutive input rows, so every output row receives one full
-// 128-byte run of codes per tile.
+// One workgroup owns a tile of kTR = 128 input rows x kTC = 256 input columns,
+// so every input row is read as one 128-byte run of codes (plus 16 scale
+// bytes) and every output row of the tile is written as one 64-byte run.
+//
+// Load phase: a thread takes a pair of input rows and one 32-column chunk,
+// dequantizes them exactly with gfx950's packed FP4 -> f32 conversion
+// (u = +-G[m] * dec(e) has at most 6 significant bits, so bf16 holds it) and
+// stores each column's two values as one dword into LDS, where tile column c
+// (= output row) is an LDS row.  The row-pair index is XOR-swizzled by the
+// column's chunk so that the stores of a wave hit distinct banks, and the LDS
+// row pitch is 68 dwords so that the 16-byte reads of the next phase are
+// conflict-free as well.
+//
+// Requantize phase: a thread owns one output row and four new 16-element
+// blocks: block amax, E4M3 scale, one Philox4x32-10 call for the block's 16
+// random bytes, then the stochastic rounding.  The floor grid point of each
+// value comes from v_cvt_scalef32_sr_pk_fp4_f32 with a zero seed (which
+// truncates to the grid toward zero, sign kept), its value from the packed
+// decode; the step up is taken iff G[lo] + k * D / 256 < |y| with D the grid
+// spacing above G[lo] (all terms exact), and values are first clamped to
+// [-6, 6] so that saturation needs no separate case.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -24,98 +35,163 @@
 
 namespace tq {
 
-constexpr int kTR = 256;  // input rows per tile (= output elements per row)
-constexpr int kTC = 64;   // input columns per tile (= output rows)
-constexpr int kSThreads = 256;
-// LDS row = one output row of the tile: kTR bf16 values as kTR/2 dwords, padded
-// so that lanes reading 16-byte runs of consecutive rows hit distinct banks.
-constexpr int kLdsStride = kTR / 2 + 4;
+constexpr int kTR = 128;          // input rows per tile (= output elements per row)
+constexpr int kTC = 256;          // input columns per tile (= output rows)
+constexpr int kSThreads = 512;
+constexpr int kLdsStride = 68;    // dwords per LDS row: 64 row pairs + 4 pad
 
-__global__ __launch_bounds__(kSThreads) void requant_transpose_sr_kernel(
+// LDS dword of tile column c, input row pair p
+__device__ __forceinline__ int lds_slot(int c, int p) { return c * kLdsStride + (p ^ (8 * (c >> 5))); }
+
+// Grid spacing above the floor point +-glo, divided by 256, from the exponent
+// bits of glo: 2^-9 below 2 (|glo| in {0, 0.5, 1, 1.5}), then half the power of
+// two of |glo| (2^-8 for 2 and 3, 2^-7 for 4 and 6).
+__device__ __forceinline__ float sr_step(float glo)
+{
+    const int e = (int)(__float_as_uint(glo) & 0x7F800000u) - (9 << 23);
+    return __int_as_float(e > 0x3B000000 ? e : 0x3B000000);
+}
+
+// Byte SEL of `w` <- the two floor codes of (a, b): v_cvt_scalef32_sr_pk_fp4_f32
+// with a zero seed and unit scale truncates each value to the grid toward zero
+// (sign kept) and leaves the other three bytes of the destination unchanged.
+// Written in asm because the compiler does not treat this destination as tied
+// to its previous value; a byte-selected write needs one wait state before the
+// register is read again (the s_nop the compiler puts after such writes).
+template <int SEL>
+__device__ __forceinline__ uint32_t floor_pk_fp4(uint32_t w, float a, float b)
+{
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 v = {a, b};
+    if (SEL == 0)
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, 0, 1.0" : "+v"(w) : "v"(v));
+    else if (SEL == 1)
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, 0, 1.0 op_sel:[0,0,1,0]\n\ts_nop 0" : "+v"(w) : "v"(v));
+    else if (SEL == 2)
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, 0, 1.0 op_sel:[0,0,0,1]\n\ts_nop 0" : "+v"(w) : "v"(v));
+    else
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, 0, 1.0 op_sel:[0,0,1,1]\n\ts_nop 0" : "+v"(w) : "v"(v));
+    return w;
+}
+
+// Stochastic rounding of eight clamped values (|yc| <= 6) with their random
+// bytes k[0..7]: floor codes from the hardware truncation, plus one where the
+// random byte falls below the distance to the floor point.
+__device__ __forceinline__ uint32_t sr_pack8(const float yc[8], const float k[8])
+{
+    uint32_t P = 0;
+    P = floor_pk_fp4<0>(P, yc[0], yc[1]);
+    P = floor_pk_fp4<1>(P, yc[2], yc[3]);
+    P = floor_pk_fp4<2>(P, yc[4], yc[5]);
+    P = floor_pk_fp4<3>(P, yc[6], yc[7]);
+    const tq_f32x2 g0 = fp4x2_to_f32<0>(P), g1 = fp4x2_to_f32<1>(P);
+    const tq_f32x2 g2 = fp4x2_to_f32<2>(P), g3 = fp4x2_to_f32<3>(P);
+    const float g[8] = {g0[0], g0[1], g1[0], g1[1], g2[0], g2[1], g3[0], g3[1]};
+    uint32_t U = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float t = __builtin_fmaf(k[i], sr_step(g[i]), fabsf(g[i]));  // exact: no rounding occurs
+        U |= (t < fabsf(yc[i])) ? (1u << (4 * i)) : 0u;
+    }
+    return clear_negative_zero(P + U);
+}
+
+__global__ __launch_bounds__(kSThreads, 2) void requant_transpose_sr_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const float* __restrict__ tensor_scale, int64_t batch, int64_t rows, int64_t cols,
     uint32_t seed_lo, uint32_t seed_hi, uint8_t* __restrict__ codes_t,
     uint8_t* __restrict__ scales_t, float* __restrict__ tensor_scale_t, int64_t tiles_r,
-    int64_t tiles_c)
+    int64_t tiles_c, int vec_in, int vec_scale_in, int vec_out, int vec_scale_out)
 {
-    __shared__ uint32_t u_s[kTC * kLdsStride];
+    __shared__ __attribute__((aligned(16))) uint32_t u_s[kTC * kLdsStride];
     const int64_t tiles_per_tensor = tiles_r * tiles_c;
     const int64_t total_tiles = tiles_per_tensor * batch;
-    const int tid = threadIdx.x;
+    const int64_t paired = total_tiles & ~(int64_t)15;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int64_t sc_pitch = cols / 16, sct_pitch = rows / 16;
 
-    for (int64_t tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
+    for (int64_t idx = blockIdx.x; idx < total_tiles; idx += gridDim.x) {
+        // workgroups idx and idx + 8 run on the same XCD: give them the two tiles
+        // that write the two halves of the same 128-byte output runs
+        const int64_t tile = idx < paired ? (idx & ~(int64_t)15) + 2 * (idx & 7) + ((idx >> 3) & 1) : idx;
         const int64_t b = tile / tiles_per_tensor;
         const int64_t rem = tile - b * tiles_per_tensor;
-        const int64_t tr = rem / tiles_c, tc = rem - tr * tiles_c;
+        const int64_t tc = rem / tiles_r, tr = rem - tc * tiles_r;
         const int64_t r0 = tr * kTR, c0 = tc * kTC;
+        const int rows_valid = (int)(rows - r0 < kTR ? rows - r0 : kTR);  // multiples of 16
+        const int cols_valid = (int)(cols - c0 < kTC ? cols - c0 : kTC);
         if (tr == 0 && tc == 0 && tid == 0)
             tensor_scale_t[b] = tensor_scale[b];
 
-        // ---- load + exact dequant: thread owns input rows (2p, 2p+1) of the tile
-        //      and one 32-column half; it writes both rows' values of a column as
-        //      one dword, so a wave writes 64 consecutive dwords per column ----
+        // ---- load + exact dequant: input rows (2p, 2p+1), columns [32h, 32h + 32) ----
         {
-            const int p = tid & 127, half = tid >> 7;
-            const int64_t cols_valid = cols - c0 < kTC ? cols - c0 : kTC;  // multiple of 16
+            const int p = 8 * wave + (lane >> 3), h = lane & 7, cl = 32 * h;
+            int nb = (cols_valid - cl) / 16;
+            nb = nb < 0 ? 0 : (nb > 2 ? 2 : nb);
+            uint32_t w[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+            float d[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+            if (2 * p < rows_valid && nb > 0) {
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                const int cl = 32 * half + 16 * blk;  // first tile column of this block
-                uint2 q[2] = {make_uint2(0, 0), make_uint2(0, 0)};
-                float d[2] = {0.0f, 0.0f};
-                if (cl < cols_valid) {
-#pragma unroll
-                    for (int rr = 0; rr < 2; ++rr) {
-                        const int64_t gr = r0 + 2 * p + rr;
-                        if (gr < rows) {
-                            q[rr] = *reinterpret_cast<const uint2*>(
-                                codes + ((b * rows + gr) * cols + c0 + cl) / 2);
-                            d[rr] = e4m3_decode(scales[(b * rows + gr) * (cols / 16) + (c0 + cl) / 16]);
+                for (int rr = 0; rr < 2; ++rr) {
+                    const int64_t grow = b * rows + r0 + 2 * p + rr;
+                    const uint8_t* src = codes + (grow * cols + c0 + cl) / 2;
+                    if (vec_in && nb == 2) {
+                        const uint4 q = *reinterpret_cast<const uint4*>(src);
+                        w[rr][0] = q.x; w[rr][1] = q.y; w[rr][2] = q.z; w[rr][3] = q.w;
+                    } else {
+                        const uint2 q0 = *reinterpret_cast<const uint2*>(src);
+                        w[rr][0] = q0.x; w[rr][1] = q0.y;
+                        if (nb == 2) {
+                            const uint2 q1 = reinterpret_cast<const uint2*>(src)[1];
+                            w[rr][2] = q1.x; w[rr][3] = q1.y;
                         }
                     }
-                }
-                // u = +-G[m] * dec(e), exact; the two rows' values of column cl+i share one dword
-                uint32_t* dst = u_s + cl * kLdsStride + p;
-#pragma unroll
-                for (int half8 = 0; half8 < 2; ++half8) {
-                    const uint32_t w0 = half8 ? q[0].y : q[0].x;
-                    const uint32_t w1 = half8 ? q[1].y : q[1].x;
-                    tq_f32x2 a0[4], a1[4];
-                    a0[0] = fp4x2_to_f32<0>(w0); a0[1] = fp4x2_to_f32<1>(w0);
-                    a0[2] = fp4x2_to_f32<2>(w0); a0[3] = fp4x2_to_f32<3>(w0);
-                    a1[0] = fp4x2_to_f32<0>(w1); a1[1] = fp4x2_to_f32<1>(w1);
-                    a1[2] = fp4x2_to_f32<2>(w1); a1[3] = fp4x2_to_f32<3>(w1);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-                        for (int t = 0; t < 2; ++t) {
-                            const int i = 8 * half8 + 2 * j + t;
-                            dst[i * kLdsStride] = pack_hi16(a0[j][t] * d[0], a1[j][t] * d[1]);
-                        }
+                    const uint8_t* sp = scales + grow * sc_pitch + (c0 + cl) / 16;
+                    if (vec_scale_in && nb == 2) {
+                        const uint32_t s2 = *reinterpret_cast<const uint16_t*>(sp);
+                        d[rr][0] = e4m3_decode(s2 & 0xFFu);
+                        d[rr][1] = e4m3_decode(s2 >> 8);
+                    } else {
+                        d[rr][0] = e4m3_decode(sp[0]);
+                        if (nb == 2)
+                            d[rr][1] = e4m3_decode(sp[1]);
                     }
                 }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float da = d[0][j >> 1], db = d[1][j >> 1];
+                const tq_f32x2 a0 = fp4x2_to_f32<0>(w[0][j]), a1 = fp4x2_to_f32<1>(w[0][j]);
+                const tq_f32x2 a2 = fp4x2_to_f32<2>(w[0][j]), a3 = fp4x2_to_f32<3>(w[0][j]);
+                const tq_f32x2 b0 = fp4x2_to_f32<0>(w[1][j]), b1 = fp4x2_to_f32<1>(w[1][j]);
+                const tq_f32x2 b2 = fp4x2_to_f32<2>(w[1][j]), b3 = fp4x2_to_f32<3>(w[1][j]);
+                const float va[8] = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+                const float vb[8] = {b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    u_s[lds_slot(cl + 8 * j + e, p)] = pack_hi16(va[e] * da, vb[e] * db);
             }
         }
         __syncthreads();
 
-        // ---- requantize: lane -> output row c0 + lane, wave -> 4 new blocks ----
+        // ---- requantize: thread -> output row c0 + c, input rows [64 half, 64 half + 64) ----
         {
-            const int lane = tid & 63, wave = tid >> 6;
-            const int64_t oc = c0 + lane;  // output row (input column)
-            if (oc < cols) {
-                const uint32_t* urow = u_s + lane * kLdsStride;
-                uint32_t words[8];
+            const int c = tid & (kTC - 1), half = tid >> 8, h = c >> 5;
+            const int64_t oc = c0 + c;
+            if (c < cols_valid) {
+                uint32_t out[8];
                 uint32_t sc = 0;
                 int nvalid = 0;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int local = 64 * wave + 16 * q;  // first input row of the block
-                    words[2 * q] = words[2 * q + 1] = 0;
-                    if (r0 + local >= rows)
+                    const int lr = 64 * half + 16 * q;  // first local input row of the block
+                    out[2 * q] = out[2 * q + 1] = 0;
+                    if (lr >= rows_valid)
                         continue;
                     ++nvalid;
-                    const uint4 w0 = *reinterpret_cast<const uint4*>(urow + local / 2);
-                    const uint4 w1 = *reinterpret_cast<const uint4*>(urow + local / 2 + 4);
-                    const uint32_t pk[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+                    const uint4* src = reinterpret_cast<const uint4*>(u_s + c * kLdsStride + 8 * ((4 * half + q) ^ h));
+                    const uint4 v0 = src[0], v1 = src[1];
+                    const uint32_t pk[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
                     float u[16];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
@@ -129,38 +205,32 @@ __global__ __launch_bounds__(kSThreads) void requant_transpose_sr_kernel(
                     const uint32_t e = e4m3_encode(A / 6.0f);
                     sc |= e << (8 * q);
                     const float dec = e4m3_decode(e);
-                    if (dec == 0.0f)
-                        continue;
-                    const float rr = 1.0f / dec;
-                    const uint64_t beta = (uint64_t)(((b * cols + oc) * rows + r0 + local) / 16);
+                    const float rcp = 1.0f / (dec == 0.0f ? 1.0f : dec);
+                    const uint64_t beta = (uint64_t)(((b * cols + oc) * rows + r0 + lr) / 16);
                     const u32x4 rnd = philox4x32_10((uint32_t)beta, (uint32_t)(beta >> 32), 0u, 0u,
                                                     seed_lo, seed_hi);
                     const uint32_t rw[4] = {rnd.x, rnd.y, rnd.z, rnd.w};
-                    uint32_t lo = 0, hi = 0;
+                    float yc[16], k[16];
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const float y = u[i] * rr;
-                        const float k = (float)((rw[i >> 2] >> (8 * (i & 3))) & 0xFFu);
-                        const uint32_t c = e2m1_code(y, e2m1_sr_bits(fabsf(y), k));
-                        if (i < 8)
-                            lo |= c << (4 * i);
-                        else
-                            hi |= c << (4 * (i - 8));
+                        yc[i] = __builtin_amdgcn_fmed3f(u[i] * rcp, -6.0f, 6.0f);
+                        k[i] = (float)((rw[i >> 2] >> (8 * (i & 3))) & 0xFFu);
                     }
-                    words[2 * q] = lo;
-                    words[2 * q + 1] = hi;
+                    if (dec != 0.0f) {
+                        out[2 * q] = sr_pack8(yc, k);
+                        out[2 * q + 1] = sr_pack8(yc + 8, k + 8);
+                    }
                 }
-                // output row oc, input rows r0 + 64*wave ... + 16*nvalid
-                uint8_t* orow = codes_t + ((b * cols + oc) * rows + r0 + 64 * wave) / 2;
-                uint8_t* srow = scales_t + (b * cols + oc) * (rows / 16) + (r0 + 64 * wave) / 16;
-                if (nvalid == 4 && ((uintptr_t)orow & 15u) == 0) {
-                    reinterpret_cast<uint4*>(orow)[0] = make_uint4(words[0], words[1], words[2], words[3]);
-                    reinterpret_cast<uint4*>(orow)[1] = make_uint4(words[4], words[5], words[6], words[7]);
+                uint8_t* orow = codes_t + ((b * cols + oc) * rows + r0 + 64 * half) / 2;
+                uint8_t* srow = scales_t + (b * cols + oc) * sct_pitch + (r0 + 64 * half) / 16;
+                if (nvalid == 4 && vec_out) {
+                    reinterpret_cast<uint4*>(orow)[0] = make_uint4(out[0], out[1], out[2], out[3]);
+                    reinterpret_cast<uint4*>(orow)[1] = make_uint4(out[4], out[5], out[6], out[7]);
                 } else {
                     for (int q = 0; q < nvalid; ++q)
-                        reinterpret_cast<uint2*>(orow)[q] = make_uint2(words[2 * q], words[2 * q + 1]);
+                        reinterpret_cast<uint2*>(orow)[q] = make_uint2(out[2 * q], out[2 * q + 1]);
                 }
-                if (nvalid == 4 && ((uintptr_t)srow & 3u) == 0) {
+                if (nvalid == 4 && vec_scale_out) {
                     *reinterpret_cast<uint32_t*>(srow) = sc;
                 } else {
                     for (int q = 0; q < nvalid; ++q)
@@ -194,9 +264,14 @@ void launch_requant_transpose_sr(const uint8_t* codes, const uint8_t* scales,
         return;
     }
     const int64_t g = total < (1 << 20) ? total : (1 << 20);
+    const int vec_in = cols % 32 == 0;
+    const int vec_scale_in = cols % 32 == 0 && ((uintptr_t)scales & 1u) == 0;
+    const int vec_out = rows % 32 == 0;
+    const int vec_scale_out = rows % 64 == 0 && ((uintptr_t)scales_t & 3u) == 0;
     hipLaunchKernelGGL(requant_transpose_sr_kernel, dim3((unsigned)g), dim3(kSThreads), 0, s, codes,
                        scales, tensor_scale, batch, rows, cols, (uint32_t)seed,
-                       (uint32_t)(seed >> 32), codes_t, scales_t, tensor_scale_t, tiles_r, tiles_c);
+                       (uint32_t)(seed >> 32), codes_t, scales_t, tensor_scale_t, tiles_r, tiles_c,
+                       vec_in, vec_scale_in, vec_out, vec_scale_out);
 }
 
 }  // namespace tq
