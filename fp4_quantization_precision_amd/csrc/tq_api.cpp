@@ -170,7 +170,7 @@ TQ_API tq_status tq_grouped_gemm_nvfp4(const uint16_t* a, const int32_t* group_o
         return TQ_ERR_SHAPE;
     int64_t tmp;
     if (!product(m_total, k, 1, &tmp) || !product(m_total, n, 1, &tmp) ||
-        !product(num_groups, n, k, &tmp) || k % 16 != 0 || n % 2 != 0)
+        !product(num_groups, n, k, &tmp) || k % 16 != 0 || k > (int64_t(1) << 22) || n % 2 != 0)
         return TQ_ERR_SHAPE;
     if (!group_offsets)
         return TQ_ERR_NULL;

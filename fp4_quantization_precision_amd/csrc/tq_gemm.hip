@@ -21,6 +21,12 @@
 // loads of K-slice s+1 (activations, weight codes, block scales) are issued
 // before the MFMAs of slice s and only written to LDS (activations as is,
 // weights dequantized with gfx950's packed FP4 -> f32 conversion) after them.
+// All operand loads are buffer loads against per-workgroup resources: the
+// per-thread byte offsets are fixed for the whole K loop and the slice position
+// is a scalar offset, so the loop spends no vector instructions on addresses,
+// and rows past the end of A or W read as zeros in hardware (such rows only
+// feed output rows or columns that are never stored).  Only a partial last
+// K-slice (K not a multiple of 64) masks its loads in registers.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,11 +36,28 @@
 namespace tq {
 
 constexpr int kBM = 128, kBN = 128, kBK = 64, kGThreads = 256;
-constexpr int kLd = kBK + 8;            // bf16 per LDS row of an A or W tile
-constexpr int kCLd = kBN + 8;           // bf16 per LDS row of the output tile
-constexpr int kSmemHalves = 2 * kBM * kLd;  // A tile + W tile (kBM == kBN)
+#ifndef TQ_GEMM_SWZ
+#define TQ_GEMM_SWZ 1
+#endif
+constexpr int kRowPitch = TQ_GEMM_SWZ == 2 ? 144 : 128;  // bytes per LDS row of an operand tile
+constexpr int kTileBytes = kBM * kRowPitch;              // one bf16 operand tile in LDS
+constexpr int kCLd = kBN + 8;              // bf16 per LDS row of the staged output tile
 static_assert(kBM == kBN, "A and W tiles share one LDS layout");
-static_assert(kBM * kCLd <= kSmemHalves, "output tile must fit in the operand tiles' LDS");
+static_assert(kBM * kCLd * 2 <= 3 * kTileBytes, "output tile must fit in the operand tiles' LDS");
+
+// Byte offset of 16-byte chunk j (0..7) of LDS row r.  Rows are 128 bytes; the
+// chunk index is XORed with (r / 2) % 8, so any 16 consecutive rows read at one
+// chunk, and any 2 rows written in full, cover all 16 four-bank groups.
+__device__ __forceinline__ int swz(int r, int j)
+{
+#if TQ_GEMM_SWZ == 2
+    return r * 144 + 16 * j;
+#elif TQ_GEMM_SWZ == 0
+    return r * 128 + 16 * (j ^ (r & 7));
+#else
+    return r * 128 + 16 * (j ^ ((r >> 1) & 7));
+#endif
+}
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -56,21 +79,30 @@ __device__ __forceinline__ uint4 dequant8_bf16(uint32_t w, float d)
                       pack_hi16(p2[0] * d, p2[1] * d), pack_hi16(p3[0] * d, p3[1] * d));
 }
 
-struct TileRegs {
+struct ARegs {
     uint4 a[4];   // 4 x 8 bf16 of the A tile
-    uint4 w;      // 32 weight codes (one row, 32 consecutive k)
-    float d[2];   // their two block scales
 };
+struct WRegs {
+    uint4 w;      // 32 weight codes (one row, 32 consecutive k)
+    uint32_t s;   // their two E4M3 block scales (low 16 bits)
+};
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint4 to_uint4(u32x4_t v) { return make_uint4(v[0], v[1], v[2], v[3]); }
 
 __global__ __launch_bounds__(kGThreads, 3) void grouped_gemm_nvfp4_kernel(
     const uint16_t* __restrict__ a, const int32_t* __restrict__ group_offsets, int num_groups,
-    int64_t n, int64_t k, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales,
-    const float* __restrict__ w_tensor_scale, uint16_t* __restrict__ out, int n_tiles)
+    int64_t m_total, int64_t n, int64_t k, const uint8_t* __restrict__ w_codes,
+    const uint8_t* __restrict__ w_scales, const float* __restrict__ w_tensor_scale,
+    uint16_t* __restrict__ out, int n_tiles)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[kSmemHalves];
+    // A tile, then two dequantized W tiles (the one being read, the one being filled)
+    __shared__ __attribute__((aligned(16))) uint8_t smem[3 * kTileBytes];
     __shared__ int64_t s_tile[3];
-    uint16_t* As = smem;
-    uint16_t* Ws = smem + kBM * kLd;
+    uint8_t* As = smem;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -145,50 +177,86 @@ __global__ __launch_bounds__(kGThreads, 3) void grouped_gemm_nvfp4_kernel(
     const int64_t col0 = s_tile[2] * kBN;
     const int64_t kb = k / 16;  // scale blocks per weight row
 
-    // per-thread load coordinates
+    // per-workgroup buffer resources over the tile's rows of A and W (and W's
+    // scales); loads past num_records return zeros
+    const int64_t a_rows = m_total - row0 < kBM ? m_total - row0 : kBM;
+    const int64_t w_rows = n - col0 < kBN ? n - col0 : kBN;
+    const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a + row0 * k), 0, (int)(a_rows * k * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(w_codes + (e * n + col0) * (k / 2)), 0, (int)(w_rows * (k / 2)), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(w_scales + (e * n + col0) * kb), 0, (int)(w_rows * kb), 0x00020000);
+    // per-thread byte offsets: A pieces (row r, 8 k at c8), one weight row half
+    int voff_a[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int idx = tid + it * kGThreads;
+        voff_a[it] = ((idx >> 3) * (int)k + 8 * (idx & 7)) * 2;
+    }
     const int wn_row = tid >> 1, wk_half = tid & 1;  // weight row in tile, 32-k half
-    const int64_t w_row = e * n + col0 + wn_row;
-    const bool w_row_ok = col0 + wn_row < n;
+    const int voff_w = wn_row * (int)(k / 2) + 16 * wk_half;
+    const int voff_s = wn_row * (int)kb + 2 * wk_half;
 
-    auto load = [&](int64_t k0, TileRegs& R) {
+    // K-slices: when K is not a multiple of 64 the partial slice [0, K % 64) comes
+    // first and is loaded (masked) before the loop; every slice the loop loads is
+    // full, so the loop issues the same loads every time, and a slice past the
+    // end is loaded with an out-of-range scalar offset, which reads zeros.
+    const int64_t r_tail = k % kBK;
+    const int64_t steps = k / kBK + (r_tail ? 1 : 0);
+    auto kofs = [&](int64_t t) -> int64_t {
+        return r_tail ? (t == 0 ? 0 : r_tail + kBK * (t - 1)) : kBK * t;
+    };
+    constexpr int kOutOfRange = 0x7FFFFF00;  // + any per-thread offset: beyond num_records
+    auto load_a = [&](int64_t t, ARegs& R) {
+        const int so = t < steps ? (int)(kofs(t) * 2) : kOutOfRange;
+#pragma unroll
+        for (int it = 0; it < 4; ++it)
+            R.a[it] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs_a, voff_a[it], so, 0));
+    };
+    auto load_w = [&](int64_t t, WRegs& R) {
+        const bool ok = t < steps;
+        const int so_w = ok ? (int)(kofs(t) / 2) : kOutOfRange;
+        const int so_s = ok ? (int)(kofs(t) / 16) : kOutOfRange;
+        R.w = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs_w, voff_w, so_w, 0));
+        R.s = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_s, voff_s, so_s, 0) |
+              ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_s, voff_s + 1, so_s, 0) << 8);
+    };
+    // the partial first slice: activations at or beyond K % 64 are zeroed, weights
+    // are loaded block by block (a 16-byte load could run past the row)
+    auto load_partial = [&](ARegs& RA_, WRegs& RW_) {
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-            const int idx = tid + it * kGThreads;
-            const int r = idx >> 3, c8 = idx & 7;
-            const int64_t gr = row0 + r, gk = k0 + 8 * c8;
-            R.a[it] = (gr < row_end && gk < k) ? *reinterpret_cast<const uint4*>(a + gr * k + gk)
-                                               : make_uint4(0, 0, 0, 0);
+            RA_.a[it] = make_uint4(0, 0, 0, 0);
+            if (8 * ((tid + it * kGThreads) & 7) < r_tail)
+                RA_.a[it] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs_a, voff_a[it], 0, 0));
         }
-        const int64_t gk = k0 + 32 * wk_half;
-        R.w = make_uint4(0, 0, 0, 0);
-        R.d[0] = R.d[1] = 0.0f;
-        if (w_row_ok) {
-            const uint8_t* wp = w_codes + (w_row * k + gk) / 2;
-            if (gk + 32 <= k) {
-                const uint2 lo = *reinterpret_cast<const uint2*>(wp);
-                const uint2 hi = *reinterpret_cast<const uint2*>(wp + 8);
-                R.w = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                R.d[0] = e4m3_decode(w_scales[w_row * kb + gk / 16]);
-                R.d[1] = e4m3_decode(w_scales[w_row * kb + gk / 16 + 1]);
-            } else if (gk + 16 <= k) {
-                const uint2 lo = *reinterpret_cast<const uint2*>(wp);
-                R.w = make_uint4(lo.x, lo.y, 0, 0);
-                R.d[0] = e4m3_decode(w_scales[w_row * kb + gk / 16]);
-            }
+        RW_.w = make_uint4(0, 0, 0, 0);
+        RW_.s = 0;
+        if (32 * wk_half < r_tail) {
+            const u32x2_t lo = __builtin_amdgcn_raw_buffer_load_b64(rs_w, voff_w, 0, 0);
+            RW_.w.x = lo[0];
+            RW_.w.y = lo[1];
+            RW_.s = __builtin_amdgcn_raw_buffer_load_b8(rs_s, voff_s, 0, 0);
+        }
+        if (32 * wk_half + 16 < r_tail) {
+            const u32x2_t hi = __builtin_amdgcn_raw_buffer_load_b64(rs_w, voff_w + 8, 0, 0);
+            RW_.w.z = hi[0];
+            RW_.w.w = hi[1];
+            RW_.s |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_s, voff_s + 1, 0, 0) << 8;
         }
     };
-    auto store = [&](const TileRegs& R) {
+    auto store_a = [&](const ARegs& R) {
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
             const int idx = tid + it * kGThreads;
-            const int r = idx >> 3, c8 = idx & 7;
-            *reinterpret_cast<uint4*>(As + r * kLd + 8 * c8) = R.a[it];
+            *reinterpret_cast<uint4*>(As + swz(idx >> 3, idx & 7)) = R.a[it];
         }
-        uint4* dst = reinterpret_cast<uint4*>(Ws + wn_row * kLd + 32 * wk_half);
-        dst[0] = dequant8_bf16(R.w.x, R.d[0]);
-        dst[1] = dequant8_bf16(R.w.y, R.d[0]);
-        dst[2] = dequant8_bf16(R.w.z, R.d[1]);
-        dst[3] = dequant8_bf16(R.w.w, R.d[1]);
+    };
+    // one quarter (8 codes) of this thread's weight row piece, dequantized into buffer Wd
+    auto dequant_quarter = [&](const WRegs& R, f32x2_t d, int q, uint8_t* Wd) {
+        const uint32_t w = q == 0 ? R.w.x : (q == 1 ? R.w.y : (q == 2 ? R.w.z : R.w.w));
+        *reinterpret_cast<uint4*>(Wd + swz(wn_row, 4 * wk_half + q)) = dequant8_bf16(w, q < 2 ? d[0] : d[1]);
     };
 
     const int wm = wave >> 1, wn = wave & 1;
@@ -201,27 +269,49 @@ __global__ __launch_bounds__(kGThreads, 3) void grouped_gemm_nvfp4_kernel(
             for (int r = 0; r < 16; ++r)
                 acc[i][j][r] = 0.0f;
 
-    TileRegs R;
-    if (k > 0) {
-        load(0, R);
-        store(R);
+    // Slice t reads A from As and W from buffer t % 2.  During slice t the
+    // activations of t + 1 and the weight codes of t + 2 are in flight, and the
+    // codes of t + 1 (loaded one slice earlier) are dequantized into the other W
+    // buffer between the MFMAs.
+    ARegs RA;
+    WRegs RW, RW2 = {make_uint4(0, 0, 0, 0), 0u};
+    if (steps > 0) {
+        if (r_tail) {
+            load_partial(RA, RW);
+        } else {
+            load_a(0, RA);
+            load_w(0, RW);
+        }
+        store_a(RA);
+        const f32x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(RW.s, 1.0f, false);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            dequant_quarter(RW, d, q, smem + kTileBytes);
+        load_w(1, RW);
     }
     __syncthreads();
-    for (int64_t k0 = 0; k0 < k; k0 += kBK) {
-        const bool more = k0 + kBK < k;
-        if (more)
-            load(k0 + kBK, R);
+    // one K-slice; `cur` holds the codes of slice t + 1, `nxt` receives those of t + 2
+    auto step = [&](int64_t t, const WRegs& cur, WRegs& nxt) {
+        const bool more = t + 1 < steps;
+        load_a(t + 1, RA);
+        load_w(t + 2, nxt);
+        const uint8_t* Wc = smem + kTileBytes * (1 + (int)(t & 1));
+        uint8_t* Wn = smem + kTileBytes * (2 - (int)(t & 1));
+        const f32x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cur.s, 1.0f, false);
 #pragma unroll
         for (int kk = 0; kk < kBK / 16; ++kk) {
+            const int ch = 2 * kk + (lane >> 5);
             bf16x8_t af[2], bfr[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
                 af[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                    As + (64 * wm + 32 * i + (lane & 31)) * kLd + 16 * kk + 8 * (lane >> 5)));
+                    As + swz(64 * wm + 32 * i + (lane & 31), ch)));
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 bfr[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                    Ws + (64 * wn + 32 * j + (lane & 31)) * kLd + 16 * kk + 8 * (lane >> 5)));
+                    Wc + swz(64 * wn + 32 * j + (lane & 31), ch)));
+            if (more)
+                dequant_quarter(cur, d, kk, Wn);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -230,14 +320,20 @@ __global__ __launch_bounds__(kGThreads, 3) void grouped_gemm_nvfp4_kernel(
         }
         __syncthreads();
         if (more) {
-            store(R);
+            store_a(RA);
             __syncthreads();
         }
+    };
+    // two slices per trip so that the two code registers swap roles without copies
+    for (int64_t t = 0; t < steps; t += 2) {
+        step(t, RW, RW2);
+        if (t + 1 < steps)
+            step(t + 1, RW2, RW);
     }
 
     // ---- epilogue: scale, RNE to bf16, stage the tile in LDS, coalesced stores ----
     const float s_e = w_tensor_scale[e];
-    uint16_t* Cs = smem;
+    uint16_t* Cs = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -282,8 +378,8 @@ void launch_grouped_gemm_nvfp4(const uint16_t* a, const int32_t* group_offsets, 
     // a multiple of 8 with at least ceil(total/8) groups per XCD slot
     grid = ((grid + 7) / 8) * 8;
     hipLaunchKernelGGL(grouped_gemm_nvfp4_kernel, dim3((unsigned)grid), dim3(kGThreads), 0, s, a,
-                       group_offsets, num_groups, n, k, w_codes, w_scales, w_tensor_scale, out,
-                       n_tiles);
+                       group_offsets, num_groups, m_total, n, k, w_codes, w_scales, w_tensor_scale,
+                       out, n_tiles);
 }
 
 }  // namespace tq

@@ -121,6 +121,7 @@ def test_gemm_validation(L):
 
     assert call(g=0) == TQ_ERR_SHAPE
     assert call(k=40) == TQ_ERR_SHAPE
+    assert call(k=(1 << 22) + 16) == TQ_ERR_SHAPE
     assert call(n=63) == TQ_ERR_SHAPE
     assert call(m=-1) == TQ_ERR_SHAPE
     assert call(off=NULL) == TQ_ERR_NULL
