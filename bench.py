@@ -315,6 +315,15 @@ KERNEL_OF = {
 # 1 GiB device copy of --copy-calibration), keyed by the SHA-256 of the kernel's
 # source file when the counters were taken: a changed source reports null.
 TRAFFIC = {
+    # FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0: the 1 GiB copy read 524314 KiB fetched and
+    # 1048576 KiB written
+    "amax": {"bytes": 201424606, "fetch_kib": 98324.7, "write_kib": 64.0, "source_sha256": "66319b0f5043f16cbdb70f34304eb9a8013ce2db44bd76cec51d8ef03134c7a9"},
+    "quantize": {"bytes": 258644038, "fetch_kib": 98514.9, "write_kib": 55562.0, "source_sha256": "66319b0f5043f16cbdb70f34304eb9a8013ce2db44bd76cec51d8ef03134c7a9"},
+    "quantize_hint": {"bytes": 270930032, "fetch_kib": 98358.1, "write_kib": 67873.5, "source_sha256": "66319b0f5043f16cbdb70f34304eb9a8013ce2db44bd76cec51d8ef03134c7a9"},
+    "guided": {"bytes": 270629404, "fetch_kib": 104488.0, "write_kib": 55320.8, "source_sha256": "66319b0f5043f16cbdb70f34304eb9a8013ce2db44bd76cec51d8ef03134c7a9"},
+    "mismatch": {"bytes": 100793827, "fetch_kib": 49175.5, "write_kib": 85.3, "source_sha256": "66319b0f5043f16cbdb70f34304eb9a8013ce2db44bd76cec51d8ef03134c7a9"},
+    "sr_transpose": {"bytes": 119785807, "fetch_kib": 27765.2, "write_kib": 61450.7, "source_sha256": "dcf2bfeab6b2b11b602f702b4ef2b00763b153aa944cb93966c0445030938e90"},
+    "gemm": {"bytes": 156472214, "fetch_kib": 43636.6, "write_kib": 65536.0, "source_sha256": "7452e0712dcf97d0d118cc803c6615c432d3d803cc27726d843f7efece17d509"},
 }
 
 
