@@ -8,14 +8,16 @@
 // the per-expert fp32 tensor scale is applied once in the epilogue before the
 // round-to-nearest-even conversion to bf16.
 //
-// Work decomposition.  One workgroup (4 waves) computes a kBM x kBN output tile
-// of one group (expert); each wave owns a 64 x 64 sub-tile = 2 x 2 MFMA
-// 32x32x16 tiles.  The tile list is derived on the device from the group
-// offsets (a wave-wide prefix sum of per-group tile counts), so no host
-// synchronisation is needed.  Consecutive workgroup ids are dealt round-robin
-// to the 8 XCDs; the id -> tile map undoes that, so each XCD walks a contiguous
-// run of tiles in (M-tile, N-tile) order and the N-tiles of one M-tile share
-// their activation rows through that XCD's L2.
+// Work decomposition.  One workgroup (4 waves) computes a kBM x kBN = 128 x 256
+// output tile of one group (expert); each wave owns a 64 x 128 sub-tile of 2 x 4
+// MFMA 32x32x16 tiles, which reads 0.75 KiB of LDS fragments per MFMA (1 KiB at
+// 64 x 64); LDS fragment bandwidth, not the MFMA rate, is what bounds this loop.
+// The tile list is derived on the device from the group offsets (a wave-wide
+// prefix sum of per-group tile counts), so no host synchronisation is needed.
+// Consecutive workgroup ids are dealt round-robin to the 8 XCDs; the id -> tile
+// map undoes that, so each XCD walks a contiguous run of tiles in (M-tile,
+// N-tile) order and the N-tiles of one M-tile share their activation rows
+// through that XCD's L2.
 //
 // Pipeline.  The K loop is software-pipelined through registers: the global
 // loads of K-slice s+1 (activations, weight codes, block scales) are issued
@@ -35,15 +37,22 @@
 
 namespace tq {
 
-constexpr int kBM = 128, kBN = 128, kBK = 64, kGThreads = 256;
+#ifndef TQ_GEMM_BN
+#define TQ_GEMM_BN 256
+#endif
+constexpr int kBM = 128, kBN = TQ_GEMM_BN, kBK = 64, kGThreads = 256;
 #ifndef TQ_GEMM_SWZ
 #define TQ_GEMM_SWZ 1
 #endif
 constexpr int kRowPitch = TQ_GEMM_SWZ == 2 ? 144 : 128;  // bytes per LDS row of an operand tile
-constexpr int kTileBytes = kBM * kRowPitch;              // one bf16 operand tile in LDS
-constexpr int kCLd = kBN + 8;              // bf16 per LDS row of the staged output tile
-static_assert(kBM == kBN, "A and W tiles share one LDS layout");
-static_assert(kBM * kCLd * 2 <= 3 * kTileBytes, "output tile must fit in the operand tiles' LDS");
+constexpr int kATile = kBM * kRowPitch;                  // bf16 activation tile in LDS
+constexpr int kWTile = kBN * kRowPitch;                  // dequantized weight tile in LDS
+constexpr int kSmem = kATile + 2 * kWTile;
+constexpr int kCLd = kBN + 8;                            // bf16 per LDS row of the staged output
+constexpr int kWPieces = kBN / 128;                      // 32-k weight pieces per thread per slice
+constexpr int kNJ = kBN / 64;                            // MFMA tiles per wave along N
+constexpr int kOcc = kBN == 128 ? 3 : 2;                 // workgroups per CU
+static_assert(kBM * kCLd * 2 <= kSmem, "output tile must fit in the operand tiles' LDS");
 
 // Byte offset of 16-byte chunk j (0..7) of LDS row r.  Rows are 128 bytes; the
 // chunk index is XORed with (r / 2) % 8, so any 16 consecutive rows read at one
@@ -83,8 +92,8 @@ struct ARegs {
     uint4 a[4];   // 4 x 8 bf16 of the A tile
 };
 struct WRegs {
-    uint4 w;      // 32 weight codes (one row, 32 consecutive k)
-    uint32_t s;   // their two E4M3 block scales (low 16 bits)
+    uint4 w[kWPieces];     // per piece: 32 weight codes (one row, 32 consecutive k)
+    uint32_t s[kWPieces];  // per piece: its two E4M3 block scales (low 16 bits)
 };
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
@@ -93,15 +102,17 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint4 to_uint4(u32x4_t v) { return make_uint4(v[0], v[1], v[2], v[3]); }
 
-__global__ __launch_bounds__(kGThreads, 3) void grouped_gemm_nvfp4_kernel(
+__global__ __launch_bounds__(kGThreads, kOcc) void grouped_gemm_nvfp4_kernel(
     const uint16_t* __restrict__ a, const int32_t* __restrict__ group_offsets, int num_groups,
     int64_t m_total, int64_t n, int64_t k, const uint8_t* __restrict__ w_codes,
     const uint8_t* __restrict__ w_scales, const float* __restrict__ w_tensor_scale,
     uint16_t* __restrict__ out, int n_tiles)
 {
-    // A tile, then two dequantized W tiles (the one being read, the one being filled)
-    __shared__ __attribute__((aligned(16))) uint8_t smem[3 * kTileBytes];
-    __shared__ int64_t s_tile[3];
+    // A tile, then two dequantized W tiles (the one being read, the one being filled).
+    // The tile id is passed through the start of the second W tile, which is first
+    // written after the prologue's barrier.
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
+    int64_t* s_tile = reinterpret_cast<int64_t*>(smem + kATile + kWTile);
     uint8_t* As = smem;
 
     const int tid = threadIdx.x;
@@ -194,9 +205,15 @@ __global__ __launch_bounds__(kGThreads, 3) void grouped_gemm_nvfp4_kernel(
         const int idx = tid + it * kGThreads;
         voff_a[it] = ((idx >> 3) * (int)k + 8 * (idx & 7)) * 2;
     }
-    const int wn_row = tid >> 1, wk_half = tid & 1;  // weight row in tile, 32-k half
-    const int voff_w = wn_row * (int)(k / 2) + 16 * wk_half;
-    const int voff_s = wn_row * (int)kb + 2 * wk_half;
+    // weight pieces: piece q = tid + 256 p covers row q / 2, k half q % 2 of the slice
+    int wn_row[kWPieces], voff_w[kWPieces], voff_s[kWPieces];
+    const int wk_half = tid & 1;
+#pragma unroll
+    for (int p = 0; p < kWPieces; ++p) {
+        wn_row[p] = (tid + kGThreads * p) >> 1;
+        voff_w[p] = wn_row[p] * (int)(k / 2) + 16 * wk_half;
+        voff_s[p] = wn_row[p] * (int)kb + 2 * wk_half;
+    }
 
     // K-slices: when K is not a multiple of 64 the partial slice [0, K % 64) comes
     // first and is loaded (masked) before the loop; every slice the loop loads is
@@ -218,9 +235,12 @@ __global__ __launch_bounds__(kGThreads, 3) void grouped_gemm_nvfp4_kernel(
         const bool ok = t < steps;
         const int so_w = ok ? (int)(kofs(t) / 2) : kOutOfRange;
         const int so_s = ok ? (int)(kofs(t) / 16) : kOutOfRange;
-        R.w = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs_w, voff_w, so_w, 0));
-        R.s = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_s, voff_s, so_s, 0) |
-              ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_s, voff_s + 1, so_s, 0) << 8);
+#pragma unroll
+        for (int p = 0; p < kWPieces; ++p) {
+            R.w[p] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs_w, voff_w[p], so_w, 0));
+            R.s[p] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_s, voff_s[p], so_s, 0) |
+                     ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_s, voff_s[p] + 1, so_s, 0) << 8);
+        }
     };
     // the partial first slice: activations at or beyond K % 64 are zeroed, weights
     // are loaded block by block (a 16-byte load could run past the row)
@@ -231,19 +251,22 @@ __global__ __launch_bounds__(kGThreads, 3) void grouped_gemm_nvfp4_kernel(
             if (8 * ((tid + it * kGThreads) & 7) < r_tail)
                 RA_.a[it] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs_a, voff_a[it], 0, 0));
         }
-        RW_.w = make_uint4(0, 0, 0, 0);
-        RW_.s = 0;
-        if (32 * wk_half < r_tail) {
-            const u32x2_t lo = __builtin_amdgcn_raw_buffer_load_b64(rs_w, voff_w, 0, 0);
-            RW_.w.x = lo[0];
-            RW_.w.y = lo[1];
-            RW_.s = __builtin_amdgcn_raw_buffer_load_b8(rs_s, voff_s, 0, 0);
-        }
-        if (32 * wk_half + 16 < r_tail) {
-            const u32x2_t hi = __builtin_amdgcn_raw_buffer_load_b64(rs_w, voff_w + 8, 0, 0);
-            RW_.w.z = hi[0];
-            RW_.w.w = hi[1];
-            RW_.s |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_s, voff_s + 1, 0, 0) << 8;
+#pragma unroll
+        for (int p = 0; p < kWPieces; ++p) {
+            RW_.w[p] = make_uint4(0, 0, 0, 0);
+            RW_.s[p] = 0;
+            if (32 * wk_half < r_tail) {
+                const u32x2_t lo = __builtin_amdgcn_raw_buffer_load_b64(rs_w, voff_w[p], 0, 0);
+                RW_.w[p].x = lo[0];
+                RW_.w[p].y = lo[1];
+                RW_.s[p] = __builtin_amdgcn_raw_buffer_load_b8(rs_s, voff_s[p], 0, 0);
+            }
+            if (32 * wk_half + 16 < r_tail) {
+                const u32x2_t hi = __builtin_amdgcn_raw_buffer_load_b64(rs_w, voff_w[p] + 8, 0, 0);
+                RW_.w[p].z = hi[0];
+                RW_.w[p].w = hi[1];
+                RW_.s[p] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_s, voff_s[p] + 1, 0, 0) << 8;
+            }
         }
     };
     auto store_a = [&](const ARegs& R) {
@@ -253,18 +276,20 @@ __global__ __launch_bounds__(kGThreads, 3) void grouped_gemm_nvfp4_kernel(
             *reinterpret_cast<uint4*>(As + swz(idx >> 3, idx & 7)) = R.a[it];
         }
     };
-    // one quarter (8 codes) of this thread's weight row piece, dequantized into buffer Wd
-    auto dequant_quarter = [&](const WRegs& R, f32x2_t d, int q, uint8_t* Wd) {
-        const uint32_t w = q == 0 ? R.w.x : (q == 1 ? R.w.y : (q == 2 ? R.w.z : R.w.w));
-        *reinterpret_cast<uint4*>(Wd + swz(wn_row, 4 * wk_half + q)) = dequant8_bf16(w, q < 2 ? d[0] : d[1]);
+    // one quarter (8 codes) of weight piece p, dequantized into buffer Wd
+    auto dequant_quarter = [&](const WRegs& R, int p, int q, uint8_t* Wd) {
+        const f32x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(R.s[p], 1.0f, false);
+        const uint32_t w = q == 0 ? R.w[p].x : (q == 1 ? R.w[p].y : (q == 2 ? R.w[p].z : R.w[p].w));
+        *reinterpret_cast<uint4*>(Wd + swz(wn_row[p], 4 * wk_half + q)) =
+            dequant8_bf16(w, q < 2 ? d[0] : d[1]);
     };
 
     const int wm = wave >> 1, wn = wave & 1;
-    f32x16_t acc[2][2];
+    f32x16_t acc[2][kNJ];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < kNJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 acc[i][j][r] = 0.0f;
@@ -274,7 +299,7 @@ __global__ __launch_bounds__(kGThreads, 3) void grouped_gemm_nvfp4_kernel(
     // codes of t + 1 (loaded one slice earlier) are dequantized into the other W
     // buffer between the MFMAs.
     ARegs RA;
-    WRegs RW, RW2 = {make_uint4(0, 0, 0, 0), 0u};
+    WRegs RW, RW2 = {};
     if (steps > 0) {
         if (r_tail) {
             load_partial(RA, RW);
@@ -283,10 +308,11 @@ __global__ __launch_bounds__(kGThreads, 3) void grouped_gemm_nvfp4_kernel(
             load_w(0, RW);
         }
         store_a(RA);
-        const f32x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(RW.s, 1.0f, false);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            dequant_quarter(RW, d, q, smem + kTileBytes);
+        for (int p = 0; p < kWPieces; ++p)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                dequant_quarter(RW, p, q, smem + kATile);
         load_w(1, RW);
     }
     __syncthreads();
@@ -295,27 +321,29 @@ __global__ __launch_bounds__(kGThreads, 3) void grouped_gemm_nvfp4_kernel(
         const bool more = t + 1 < steps;
         load_a(t + 1, RA);
         load_w(t + 2, nxt);
-        const uint8_t* Wc = smem + kTileBytes * (1 + (int)(t & 1));
-        uint8_t* Wn = smem + kTileBytes * (2 - (int)(t & 1));
-        const f32x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(cur.s, 1.0f, false);
+        const uint8_t* Wc = smem + kATile + kWTile * (int)(t & 1);
+        uint8_t* Wn = smem + kATile + kWTile * (1 - (int)(t & 1));
 #pragma unroll
         for (int kk = 0; kk < kBK / 16; ++kk) {
             const int ch = 2 * kk + (lane >> 5);
-            bf16x8_t af[2], bfr[2];
+            bf16x8_t af[2], bfr[kNJ];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
                 af[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
                     As + swz(64 * wm + 32 * i + (lane & 31), ch)));
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < kNJ; ++j)
                 bfr[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                    Wc + swz(64 * wn + 32 * j + (lane & 31), ch)));
-            if (more)
-                dequant_quarter(cur, d, kk, Wn);
+                    Wc + swz((kBN / 2) * wn + 32 * j + (lane & 31), ch)));
+            if (more) {
+#pragma unroll
+                for (int p = 0; p < kWPieces; ++p)
+                    dequant_quarter(cur, p, kk, Wn);
+            }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < kNJ; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
         __syncthreads();
@@ -337,11 +365,11 @@ __global__ __launch_bounds__(kGThreads, 3) void grouped_gemm_nvfp4_kernel(
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < kNJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const int col = 64 * wn + 32 * j + (lane & 31);
+                const int col = (kBN / 2) * wn + 32 * j + (lane & 31);
                 Cs[row * kCLd + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][r] * s_e);
             }
     __syncthreads();
