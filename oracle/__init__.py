@@ -74,6 +74,7 @@ def lib():
         L.tqo_sr_index.restype = i32
         L.tqo_requant_transpose_sr.argtypes = [p, p, p, i64, i64, i64, C.c_uint64, p, p, p]
         L.tqo_grouped_gemm.argtypes = [p, p, C.c_int32, i64, i64, p, p, p, p, i64, p, p]
+        L.tqo_grouped_gemm_w4a4.argtypes = [p, p, p, p, C.c_int32, i64, i64, p, p, p, p, i64, p, p]
         L.tqo_code_mismatch.argtypes = [p, p, i64, i64, p]
         L.tqo_e4m3_encode_array.argtypes = [p, i64, p]
         L.tqo_e2m1_nearest_array.argtypes = [p, i64, p]
@@ -247,6 +248,26 @@ def grouped_gemm(a, group_offsets, n: int, k: int, w_codes, w_scales, w_tensor_s
     asum = np.zeros((rows.size, n), np.float64)
     lib().tqo_grouped_gemm(_ptr(A), _ptr(off), off.size - 1, n, k, _ptr(wc), _ptr(ws), _ptr(wt),
                            _ptr(rows), rows.size, _ptr(ref), _ptr(asum))
+    return ref, asum
+
+
+def grouped_gemm_w4a4(a_codes, a_scales, a_tensor_scale, group_offsets, n: int, k: int, w_codes,
+                      w_scales, w_tensor_scale, rows=None):
+    """fp64 reference rows of the W4A4 grouped GEMM (activations one NVFP4 tensor
+    [m_total][k]); returns (ref, abssum) of shape [len(rows), n]."""
+    ac, as_ = _np(a_codes, np.uint8), _np(a_scales, np.uint8)
+    at = _np(a_tensor_scale, np.float32)
+    off = _np(group_offsets, np.int32)
+    wc, ws = _np(w_codes, np.uint8), _np(w_scales, np.uint8)
+    wt = _np(w_tensor_scale, np.float32)
+    m_total = ac.size * 2 // k if k else 0
+    rows = np.arange(m_total, dtype=np.int64) if rows is None else np.asarray(rows, np.int64)
+    rows = np.ascontiguousarray(rows)
+    ref = np.zeros((rows.size, n), np.float64)
+    asum = np.zeros((rows.size, n), np.float64)
+    lib().tqo_grouped_gemm_w4a4(_ptr(ac), _ptr(as_), _ptr(at), _ptr(off), off.size - 1, n, k,
+                                _ptr(wc), _ptr(ws), _ptr(wt), _ptr(rows), rows.size, _ptr(ref),
+                                _ptr(asum))
     return ref, asum
 
 

@@ -515,6 +515,47 @@ void tqo_grouped_gemm(const uint16_t *a, const int32_t *group_offsets, int32_t n
     }
 }
 
+/* W4A4 grouped GEMM: activations NVFP4 as well ([TRACE] results-table
+ * paragraph: weights, activations and KV cache all FP4 in the compared
+ * rollouts; [TML] summary box: 4-bit forward).  The activations are one NVFP4
+ * tensor [m_total][k] (codes, block scales along k, one fp32 tensor scale);
+ * each side is dequantized exactly, the product is accumulated in double:
+ *   ref[q][c] = sum_k (G[a] dec(sa) s_a) (G[w] dec(sw) s_e). */
+void tqo_grouped_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales,
+                           const float *a_tensor_scale, const int32_t *group_offsets,
+                           int32_t num_groups, int64_t n, int64_t k, const uint8_t *w_codes,
+                           const uint8_t *w_scales, const float *w_tensor_scale,
+                           const int64_t *row_ids, int64_t nrows, double *ref, double *abssum)
+{
+    for (int64_t q = 0; q < nrows; ++q) {
+        const int64_t i = row_ids[q];
+        int e = -1;
+        for (int g = 0; g < num_groups; ++g)
+            if (group_offsets[g] <= i && i < group_offsets[g + 1]) {
+                e = g;
+                break;
+            }
+        for (int64_t c = 0; c < n; ++c) {
+            double acc = 0.0, aacc = 0.0;
+            if (e >= 0) {
+                for (int64_t kk = 0; kk < k; ++kk) {
+                    double av = tqo_e2m1_value(tqo_get_code(a_codes, i * k + kk)) *
+                                tqo_e4m3_value(a_scales[i * (k / 16) + kk / 16]) *
+                                (double)a_tensor_scale[0];
+                    int64_t wi = ((int64_t)e * n + c) * k + kk;
+                    double wv = tqo_e2m1_value(tqo_get_code(w_codes, wi)) *
+                                tqo_e4m3_value(w_scales[((int64_t)e * n + c) * (k / 16) + kk / 16]) *
+                                (double)w_tensor_scale[e];
+                    acc += av * wv;
+                    aacc += fabs(av * wv);
+                }
+            }
+            ref[q * n + c] = acc;
+            abssum[q * n + c] = aacc;
+        }
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* Mismatch statistics                                                       */
 /* ------------------------------------------------------------------------ */

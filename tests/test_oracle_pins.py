@@ -655,6 +655,56 @@ def test_gemm_oracle_closed_form(orc):
     assert (asum == (np.abs(A[[0, 2, 3, 4]]).sum(axis=1) * scale)[:, None]).all()
 
 
+def test_w4a4_gemm_oracle_matches_torch_matmul(orc):
+    """Activations NVFP4 too: the oracle equals a float64 matmul of both operands
+    decoded independently here (grid table x torch's E4M3 decode x tensor scale)."""
+    rng = np.random.default_rng(23)
+    counts = [3, 0, 9, 4]
+    E, n, k = len(counts), 16, 64
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(off[-1])
+    ac = rng.integers(0, 256, M * k // 2, dtype=np.uint8)
+    as_ = rng.integers(0, 0x7F, M * k // 16, dtype=np.uint8)
+    at = np.float32([0.37])
+    wc = rng.integers(0, 256, E * n * k // 2, dtype=np.uint8)
+    ws = rng.integers(0, 0x7F, E * n * k // 16, dtype=np.uint8)
+    wts = rng.uniform(0.1, 2.0, E).astype(np.float32)
+    ref, asum = orc.grouped_gemm_w4a4(ac, as_, at, off, n, k, wc, ws, wts)
+    A = torch.from_numpy(_w_values(ac, as_, at, 1, M, k)[0])
+    W = torch.from_numpy(_w_values(wc, ws, wts, E, n, k))
+    for e in range(E):
+        lo, hi = off[e], off[e + 1]
+        if hi == lo:
+            continue
+        want = torch.matmul(A[lo:hi], W[e].T).numpy()
+        wabs = torch.matmul(A[lo:hi].abs(), W[e].T.abs()).numpy()
+        assert np.allclose(ref[lo:hi], want, rtol=0, atol=1e-12 * max(1.0, wabs.max()))
+        assert np.allclose(asum[lo:hi], wabs, rtol=1e-12, atol=0)
+
+
+def test_w4a4_gemm_reduces_to_w4a16(orc):
+    """With a power-of-two activation tensor scale every dequantized activation is
+    exact in bf16, so the W4A4 result equals the (pinned) bf16-activation GEMM on
+    those bf16 values, bit for bit."""
+    rng = np.random.default_rng(29)
+    counts = [6, 2, 0, 5]
+    E, n, k = len(counts), 8, 48
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(off[-1])
+    ac = rng.integers(0, 256, M * k // 2, dtype=np.uint8)
+    as_ = rng.integers(0, 0x7F, M * k // 16, dtype=np.uint8)
+    at = np.float32([0.25])
+    wc = rng.integers(0, 256, E * n * k // 2, dtype=np.uint8)
+    ws = rng.integers(0, 0x7F, E * n * k // 16, dtype=np.uint8)
+    wts = rng.uniform(0.1, 2.0, E).astype(np.float32)
+    A = _w_values(ac, as_, at, 1, M, k)[0]
+    a_bf16 = torch.from_numpy(A.astype(np.float32)).to(torch.bfloat16)
+    assert np.array_equal(a_bf16.double().numpy(), A)  # exact in bf16
+    ref4, asum4 = orc.grouped_gemm_w4a4(ac, as_, at, off, n, k, wc, ws, wts)
+    ref16, asum16 = orc.grouped_gemm(a_bf16, off, n, k, wc, ws, wts)
+    assert np.array_equal(ref4, ref16) and np.array_equal(asum4, asum16)
+
+
 # ----------------------------------------------------------------------------------
 # Mismatch statistics
 # ----------------------------------------------------------------------------------
