@@ -186,6 +186,34 @@ TQ_API tq_status tq_grouped_gemm_nvfp4(const uint16_t* a, const int32_t* group_o
     return launch_status();
 }
 
+TQ_API tq_status tq_grouped_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales,
+                                      const float* a_tensor_scale, const int32_t* group_offsets,
+                                      int32_t num_groups, int64_t m_total, int64_t n, int64_t k,
+                                      const uint8_t* w_codes, const uint8_t* w_scales,
+                                      const float* w_tensor_scale, uint16_t* out, void* stream)
+{
+    if (num_groups < 1)
+        return TQ_ERR_SHAPE;
+    int64_t tmp;
+    if (!product(m_total, k, 1, &tmp) || !product(m_total, n, 1, &tmp) ||
+        !product(num_groups, n, k, &tmp) || k % 16 != 0 || k > (int64_t(1) << 22) || n % 2 != 0)
+        return TQ_ERR_SHAPE;
+    if (!group_offsets)
+        return TQ_ERR_NULL;
+    if (m_total == 0 || n == 0)
+        return TQ_OK;
+    if (!out || !w_tensor_scale || !a_tensor_scale ||
+        (k > 0 && (!a_codes || !a_scales || !w_codes || !w_scales)))
+        return TQ_ERR_NULL;
+    if (!aligned(out, 4) || (k > 0 && (!aligned(a_codes, 16) || !aligned(w_codes, 16))))
+        return TQ_ERR_ALIGN;
+    clear_error();
+    tq::launch_grouped_gemm_w4a4(a_codes, a_scales, a_tensor_scale, group_offsets, num_groups,
+                                 m_total, n, k, w_codes, w_scales, w_tensor_scale, out,
+                                 as_stream(stream));
+    return launch_status();
+}
+
 TQ_API tq_status tq_dequantize(const uint8_t* codes, const uint8_t* scales,
                                const float* tensor_scale, int64_t batch, int64_t rows,
                                int64_t cols, float* out, void* stream)

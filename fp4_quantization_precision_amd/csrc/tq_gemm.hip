@@ -88,8 +88,16 @@ __device__ __forceinline__ uint4 dequant8_bf16(uint32_t w, float d)
                       pack_hi16(p2[0] * d, p2[1] * d), pack_hi16(p3[0] * d, p3[1] * d));
 }
 
+// Activation registers of one slice: bf16 pieces, or (NVFP4 activations) one
+// 32-k piece of one row: codes and two block scales, as for the weights.
+template <bool A_FP4>
 struct ARegs {
     uint4 a[4];   // 4 x 8 bf16 of the A tile
+};
+template <>
+struct ARegs<true> {
+    uint4 w;      // 32 activation codes (one row, 32 consecutive k)
+    uint32_t s;   // their two E4M3 block scales (low 16 bits)
 };
 struct WRegs {
     uint4 w[kWPieces];     // per piece: 32 weight codes (one row, 32 consecutive k)
@@ -102,9 +110,15 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint4 to_uint4(u32x4_t v) { return make_uint4(v[0], v[1], v[2], v[3]); }
 
+// A_FP4 = false: `a` is bf16 [m_total][k].  A_FP4 = true: `a` holds NVFP4 codes
+// [m_total][k/2] with block scales `a_scales` [m_total][k/16] and the single
+// tensor scale a_tensor_scale[0]; the activation tile is dequantized exactly into
+// LDS like the weights.
+template <bool A_FP4>
 __global__ __launch_bounds__(kGThreads, kOcc) void grouped_gemm_nvfp4_kernel(
-    const uint16_t* __restrict__ a, const int32_t* __restrict__ group_offsets, int num_groups,
-    int64_t m_total, int64_t n, int64_t k, const uint8_t* __restrict__ w_codes,
+    const void* __restrict__ a, const uint8_t* __restrict__ a_scales,
+    const float* __restrict__ a_tensor_scale, const int32_t* __restrict__ group_offsets,
+    int num_groups, int64_t m_total, int64_t n, int64_t k, const uint8_t* __restrict__ w_codes,
     const uint8_t* __restrict__ w_scales, const float* __restrict__ w_tensor_scale,
     uint16_t* __restrict__ out, int n_tiles)
 {
@@ -192,8 +206,14 @@ __global__ __launch_bounds__(kGThreads, kOcc) void grouped_gemm_nvfp4_kernel(
     // scales); loads past num_records return zeros
     const int64_t a_rows = m_total - row0 < kBM ? m_total - row0 : kBM;
     const int64_t w_rows = n - col0 < kBN ? n - col0 : kBN;
-    const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a + row0 * k), 0, (int)(a_rows * k * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_a = A_FP4
+        ? __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)a + row0 * (k / 2)), 0,
+                                            (int)(a_rows * (k / 2)), 0x00020000)
+        : __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a + row0 * k), 0,
+                                            (int)(a_rows * k * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_as = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(A_FP4 ? a_scales + row0 * kb : w_scales), 0, A_FP4 ? (int)(a_rows * kb) : 0,
+        0x00020000);
     const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(w_codes + (e * n + col0) * (k / 2)), 0, (int)(w_rows * (k / 2)), 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
@@ -205,6 +225,10 @@ __global__ __launch_bounds__(kGThreads, kOcc) void grouped_gemm_nvfp4_kernel(
         const int idx = tid + it * kGThreads;
         voff_a[it] = ((idx >> 3) * (int)k + 8 * (idx & 7)) * 2;
     }
+    // NVFP4 activations: one 32-k piece per thread, row tid / 2, k half tid % 2
+    const int an_row = tid >> 1;
+    const int voff_ac = an_row * (int)(k / 2) + 16 * (tid & 1);
+    const int voff_as = an_row * (int)kb + 2 * (tid & 1);
     // weight pieces: piece q = tid + 256 p covers row q / 2, k half q % 2 of the slice
     int wn_row[kWPieces], voff_w[kWPieces], voff_s[kWPieces];
     const int wk_half = tid & 1;
@@ -225,11 +249,20 @@ __global__ __launch_bounds__(kGThreads, kOcc) void grouped_gemm_nvfp4_kernel(
         return r_tail ? (t == 0 ? 0 : r_tail + kBK * (t - 1)) : kBK * t;
     };
     constexpr int kOutOfRange = 0x7FFFFF00;  // + any per-thread offset: beyond num_records
-    auto load_a = [&](int64_t t, ARegs& R) {
-        const int so = t < steps ? (int)(kofs(t) * 2) : kOutOfRange;
+    auto load_a = [&](int64_t t, ARegs<A_FP4>& R) {
+        if constexpr (A_FP4) {
+            const bool ok = t < steps;
+            const int so_c = ok ? (int)(kofs(t) / 2) : kOutOfRange;
+            const int so_s = ok ? (int)(kofs(t) / 16) : kOutOfRange;
+            R.w = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs_a, voff_ac, so_c, 0));
+            R.s = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_as, voff_as, so_s, 0) |
+                  ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_as, voff_as + 1, so_s, 0) << 8);
+        } else {
+            const int so = t < steps ? (int)(kofs(t) * 2) : kOutOfRange;
 #pragma unroll
-        for (int it = 0; it < 4; ++it)
-            R.a[it] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs_a, voff_a[it], so, 0));
+            for (int it = 0; it < 4; ++it)
+                R.a[it] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs_a, voff_a[it], so, 0));
+        }
     };
     auto load_w = [&](int64_t t, WRegs& R) {
         const bool ok = t < steps;
@@ -244,12 +277,29 @@ __global__ __launch_bounds__(kGThreads, kOcc) void grouped_gemm_nvfp4_kernel(
     };
     // the partial first slice: activations at or beyond K % 64 are zeroed, weights
     // are loaded block by block (a 16-byte load could run past the row)
-    auto load_partial = [&](ARegs& RA_, WRegs& RW_) {
+    auto load_partial = [&](ARegs<A_FP4>& RA_, WRegs& RW_) {
+        if constexpr (A_FP4) {
+            RA_.w = make_uint4(0, 0, 0, 0);
+            RA_.s = 0;
+            if (32 * (tid & 1) < r_tail) {
+                const u32x2_t lo = __builtin_amdgcn_raw_buffer_load_b64(rs_a, voff_ac, 0, 0);
+                RA_.w.x = lo[0];
+                RA_.w.y = lo[1];
+                RA_.s = __builtin_amdgcn_raw_buffer_load_b8(rs_as, voff_as, 0, 0);
+            }
+            if (32 * (tid & 1) + 16 < r_tail) {
+                const u32x2_t hi = __builtin_amdgcn_raw_buffer_load_b64(rs_a, voff_ac + 8, 0, 0);
+                RA_.w.z = hi[0];
+                RA_.w.w = hi[1];
+                RA_.s |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_as, voff_as + 1, 0, 0) << 8;
+            }
+        } else {
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            RA_.a[it] = make_uint4(0, 0, 0, 0);
-            if (8 * ((tid + it * kGThreads) & 7) < r_tail)
-                RA_.a[it] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs_a, voff_a[it], 0, 0));
+            for (int it = 0; it < 4; ++it) {
+                RA_.a[it] = make_uint4(0, 0, 0, 0);
+                if (8 * ((tid + it * kGThreads) & 7) < r_tail)
+                    RA_.a[it] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs_a, voff_a[it], 0, 0));
+            }
         }
 #pragma unroll
         for (int p = 0; p < kWPieces; ++p) {
@@ -269,11 +319,20 @@ __global__ __launch_bounds__(kGThreads, kOcc) void grouped_gemm_nvfp4_kernel(
             }
         }
     };
-    auto store_a = [&](const ARegs& R) {
+    auto store_a = [&](const ARegs<A_FP4>& R) {
+        if constexpr (A_FP4) {
+            const f32x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(R.s, 1.0f, false);
+            const int j0 = 4 * (tid & 1);
+            *reinterpret_cast<uint4*>(As + swz(an_row, j0 + 0)) = dequant8_bf16(R.w.x, d[0]);
+            *reinterpret_cast<uint4*>(As + swz(an_row, j0 + 1)) = dequant8_bf16(R.w.y, d[0]);
+            *reinterpret_cast<uint4*>(As + swz(an_row, j0 + 2)) = dequant8_bf16(R.w.z, d[1]);
+            *reinterpret_cast<uint4*>(As + swz(an_row, j0 + 3)) = dequant8_bf16(R.w.w, d[1]);
+        } else {
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            const int idx = tid + it * kGThreads;
-            *reinterpret_cast<uint4*>(As + swz(idx >> 3, idx & 7)) = R.a[it];
+            for (int it = 0; it < 4; ++it) {
+                const int idx = tid + it * kGThreads;
+                *reinterpret_cast<uint4*>(As + swz(idx >> 3, idx & 7)) = R.a[it];
+            }
         }
     };
     // one quarter (8 codes) of weight piece p, dequantized into buffer Wd
@@ -298,7 +357,7 @@ __global__ __launch_bounds__(kGThreads, kOcc) void grouped_gemm_nvfp4_kernel(
     // activations of t + 1 and the weight codes of t + 2 are in flight, and the
     // codes of t + 1 (loaded one slice earlier) are dequantized into the other W
     // buffer between the MFMAs.
-    ARegs RA;
+    ARegs<A_FP4> RA;
     WRegs RW, RW2 = {};
     if (steps > 0) {
         if (r_tail) {
@@ -360,7 +419,7 @@ __global__ __launch_bounds__(kGThreads, kOcc) void grouped_gemm_nvfp4_kernel(
     }
 
     // ---- epilogue: scale, RNE to bf16, stage the tile in LDS, coalesced stores ----
-    const float s_e = w_tensor_scale[e];
+    const float s_e = A_FP4 ? w_tensor_scale[e] * a_tensor_scale[0] : w_tensor_scale[e];
     uint16_t* Cs = reinterpret_cast<uint16_t*>(smem);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -393,10 +452,11 @@ __global__ __launch_bounds__(kGThreads, kOcc) void grouped_gemm_nvfp4_kernel(
     }
 }
 
-void launch_grouped_gemm_nvfp4(const uint16_t* a, const int32_t* group_offsets, int num_groups,
-                               int64_t m_total, int64_t n, int64_t k, const uint8_t* w_codes,
-                               const uint8_t* w_scales, const float* w_tensor_scale, uint16_t* out,
-                               hipStream_t s)
+template <bool A_FP4>
+static void launch_gemm(const void* a, const uint8_t* a_scales, const float* a_tensor_scale,
+                        const int32_t* group_offsets, int num_groups, int64_t m_total, int64_t n,
+                        int64_t k, const uint8_t* w_codes, const uint8_t* w_scales,
+                        const float* w_tensor_scale, uint16_t* out, hipStream_t s)
 {
     const int n_tiles = (int)((n + kBN - 1) / kBN);
     const int64_t m_tiles_max = (m_total + kBM - 1) / kBM + num_groups;
@@ -405,9 +465,28 @@ void launch_grouped_gemm_nvfp4(const uint16_t* a, const int32_t* group_offsets, 
         return;
     // a multiple of 8 with at least ceil(total/8) groups per XCD slot
     grid = ((grid + 7) / 8) * 8;
-    hipLaunchKernelGGL(grouped_gemm_nvfp4_kernel, dim3((unsigned)grid), dim3(kGThreads), 0, s, a,
-                       group_offsets, num_groups, m_total, n, k, w_codes, w_scales, w_tensor_scale,
-                       out, n_tiles);
+    hipLaunchKernelGGL(grouped_gemm_nvfp4_kernel<A_FP4>, dim3((unsigned)grid), dim3(kGThreads), 0,
+                       s, a, a_scales, a_tensor_scale, group_offsets, num_groups, m_total, n, k,
+                       w_codes, w_scales, w_tensor_scale, out, n_tiles);
+}
+
+void launch_grouped_gemm_nvfp4(const uint16_t* a, const int32_t* group_offsets, int num_groups,
+                               int64_t m_total, int64_t n, int64_t k, const uint8_t* w_codes,
+                               const uint8_t* w_scales, const float* w_tensor_scale, uint16_t* out,
+                               hipStream_t s)
+{
+    launch_gemm<false>(a, nullptr, nullptr, group_offsets, num_groups, m_total, n, k, w_codes,
+                       w_scales, w_tensor_scale, out, s);
+}
+
+void launch_grouped_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales,
+                              const float* a_tensor_scale, const int32_t* group_offsets,
+                              int num_groups, int64_t m_total, int64_t n, int64_t k,
+                              const uint8_t* w_codes, const uint8_t* w_scales,
+                              const float* w_tensor_scale, uint16_t* out, hipStream_t s)
+{
+    launch_gemm<true>(a_codes, a_scales, a_tensor_scale, group_offsets, num_groups, m_total, n, k,
+                      w_codes, w_scales, w_tensor_scale, out, s);
 }
 
 }  // namespace tq

@@ -31,5 +31,10 @@ void launch_grouped_gemm_nvfp4(const uint16_t* a, const int32_t* group_offsets, 
                                int64_t m_total, int64_t n, int64_t k, const uint8_t* w_codes,
                                const uint8_t* w_scales, const float* w_tensor_scale, uint16_t* out,
                                hipStream_t s);
+void launch_grouped_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales,
+                              const float* a_tensor_scale, const int32_t* group_offsets,
+                              int num_groups, int64_t m_total, int64_t n, int64_t k,
+                              const uint8_t* w_codes, const uint8_t* w_scales,
+                              const float* w_tensor_scale, uint16_t* out, hipStream_t s);
 
 }  // namespace tq

@@ -218,6 +218,35 @@ def grouped_gemm_nvfp4(a: torch.Tensor, group_offsets: torch.Tensor, w: NVFP4, n
     return out
 
 
+def grouped_gemm_w4a4(a: NVFP4, group_offsets: torch.Tensor, w: NVFP4, n: int, k: int,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[i] = bf16(s_a s_e * A~[i] @ W~_e^T) with the activations one NVFP4 tensor
+    [m_total, k] (tq_quantize with batch 1) and W_e stored [n][k]."""
+    for t, name in ((a.codes, "a_codes"), (a.scales, "a_scales"), (w.codes, "w_codes"),
+                    (w.scales, "w_scales")):
+        _need(t, name, (torch.uint8,))
+    _need(a.tensor_scale, "a_tensor_scale", (torch.float32,))
+    _need(w.tensor_scale, "w_tensor_scale", (torch.float32,))
+    _need(group_offsets, "group_offsets", (torch.int32,))
+    groups = group_offsets.numel() - 1
+    m_total = a.codes.numel() * 2 // k if k else 0
+    if a.codes.numel() * 2 != m_total * k or a.scales.numel() * 16 != m_total * k:
+        raise ValueError("activations must be NVFP4 [m_total, k]")
+    if w.codes.numel() != groups * n * k // 2 or w.scales.numel() != groups * n * k // 16 or \
+            w.tensor_scale.numel() != groups:
+        raise ValueError("weights do not match groups x n x k")
+    if out is None:
+        out = torch.empty((m_total, n), dtype=torch.bfloat16, device=a.codes.device)
+    _need(out, "out", (torch.bfloat16,))
+    if out.numel() != m_total * n:
+        raise ValueError("out must be [m_total, n]")
+    check(lib().tq_grouped_gemm_w4a4(_p(a.codes), _p(a.scales), _p(a.tensor_scale),
+                                     _p(group_offsets), groups, m_total, n, k, _p(w.codes),
+                                     _p(w.scales), _p(w.tensor_scale), _p(out), _stream()),
+          "tq_grouped_gemm_w4a4")
+    return out
+
+
 def dequantize(q: NVFP4, batch: int, rows: int, cols: int, out: Optional[torch.Tensor] = None):
     _need(q.codes, "codes", (torch.uint8,))
     _need(q.scales, "scales", (torch.uint8,))

@@ -210,6 +210,30 @@ TQ_API tq_status tq_grouped_gemm_nvfp4(const uint16_t* a, const int32_t* group_o
                                        uint16_t* out, void* stream);
 
 /*
+ * tq_grouped_gemm_w4a4 - MoE expert GEMM with NVFP4 weights AND NVFP4 activations
+ * ([TRACE] results-table paragraph: the compared FP4 rollouts quantize weights,
+ * activations and KV cache; [TML] summary box: the MoE forward runs in NVFP4).
+ *
+ * As tq_grouped_gemm_nvfp4, with the activations one NVFP4 tensor (as written by
+ * tq_quantize with batch 1, rows m_total, cols k):
+ *   out[i][c] = bf16_rne( (s_a * s_e) * sum_k A~[i][k] * W~_e[c][k] ),
+ * A~[i][k] = +-G[m] * dec(a_scales[i][k/16]), s_a = a_tensor_scale[0]; both operands
+ * are dequantized exactly to bf16 in on-chip memory and multiplied by bf16 MFMA
+ * with fp32 accumulation.
+ *
+ *   a_codes        [m_total][k/2] u8, 16-byte aligned.
+ *   a_scales       [m_total][k/16] u8 E4M3 (0x00..0x7E).
+ *   a_tensor_scale [1] fp32.
+ *   other arguments as tq_grouped_gemm_nvfp4.
+ * Requirements and errors as tq_grouped_gemm_nvfp4.
+ */
+TQ_API tq_status tq_grouped_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales,
+                                      const float* a_tensor_scale, const int32_t* group_offsets,
+                                      int32_t num_groups, int64_t m_total, int64_t n, int64_t k,
+                                      const uint8_t* w_codes, const uint8_t* w_scales,
+                                      const float* w_tensor_scale, uint16_t* out, void* stream);
+
+/*
  * tq_dequantize - NVFP4 -> fp32: out = (+-G[m] * dec(e)) * tensor_scale ([RLQ]
  * Fig. 2 paragraph: code x scale).  Shapes as in tq_quantize; out [batch][rows][cols]
  * fp32, 16-byte aligned.  Requires cols % 16 == 0.

@@ -33,7 +33,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ["tq_quantize", "tq_extract_hint", "tq_quantize_guided",
-                     "tq_requant_transpose_sr", "tq_grouped_gemm_nvfp4"]:
+                     "tq_requant_transpose_sr", "tq_grouped_gemm_nvfp4", "tq_grouped_gemm_w4a4"]:
         assert required in names
     assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with tq.h"
 
@@ -132,6 +132,30 @@ def test_gemm_validation(L):
     assert call(a=P_MIS) == TQ_ERR_ALIGN
     assert call(wc=P_MIS) == TQ_ERR_ALIGN
     assert call(out=C.c_void_p(0x7F0000000002)) == TQ_ERR_ALIGN
+    assert call(m=0) == TQ_OK and call(n=0) == TQ_OK
+
+
+def test_w4a4_gemm_validation(L):
+    f = L.tq_grouped_gemm_w4a4
+    ok = dict(ac=P, as_=P, at=P, off=P, g=2, m=64, n=64, k=64, wc=P, ws=P, wt=P, out=P)
+
+    def call(**kw):
+        d = dict(ok, **kw)
+        return f(d["ac"], d["as_"], d["at"], d["off"], d["g"], d["m"], d["n"], d["k"], d["wc"],
+                 d["ws"], d["wt"], d["out"], NULL)
+
+    assert call(g=0) == TQ_ERR_SHAPE
+    assert call(k=40) == TQ_ERR_SHAPE
+    assert call(k=(1 << 22) + 16) == TQ_ERR_SHAPE
+    assert call(n=63) == TQ_ERR_SHAPE
+    assert call(off=NULL) == TQ_ERR_NULL
+    assert call(ac=NULL) == TQ_ERR_NULL
+    assert call(as_=NULL) == TQ_ERR_NULL
+    assert call(at=NULL) == TQ_ERR_NULL
+    assert call(wc=NULL) == TQ_ERR_NULL
+    assert call(out=NULL) == TQ_ERR_NULL
+    assert call(ac=P_MIS) == TQ_ERR_ALIGN
+    assert call(wc=P_MIS) == TQ_ERR_ALIGN
     assert call(m=0) == TQ_OK and call(n=0) == TQ_OK
 
 

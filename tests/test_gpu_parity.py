@@ -465,6 +465,54 @@ def test_grouped_gemm_closed_form():
 # Mismatch counting
 # ----------------------------------------------------------------------------------
 
+def _w4a4_check(counts, n, k, seed=7, sample=None, strict=True):
+    """W4A4: the activations are nearest-quantized by the oracle (one tensor), the
+    weights per expert; both NVFP4 operands go to the GPU and the result is checked
+    against the oracle's float64 product of the decoded operands, to the bound of
+    the bf16-activation GEMM."""
+    G = len(counts)
+    M = int(sum(counts))
+    a, w, off = inputs.grouped_gemm_inputs(groups=G, tokens=M, k=k, n=n, device="cpu", seed=seed,
+                                           counts=counts)
+    oa = oracle.quantize(a, 1, M, k)
+    ow = oracle.quantize(w, G, n, k)
+    dev = lambda x: torch.from_numpy(x).to(DEV)
+    aq = ops.NVFP4(dev(oa["codes"]), dev(oa["scales"]), dev(oa["tensor_scale"]),
+                   torch.zeros(1, device=DEV))
+    wq = ops.NVFP4(dev(ow["codes"]), dev(ow["scales"]), dev(ow["tensor_scale"]),
+                   torch.zeros(G, device=DEV))
+    out = ops.grouped_gemm_w4a4(aq, off.to(DEV), wq, n, k)
+    torch.cuda.synchronize()
+    if sample is None:
+        rows = np.arange(M)
+    else:
+        rng = np.random.default_rng(seed)
+        o = off.numpy()
+        edges = np.concatenate([o[:-1][np.diff(o) > 0], o[1:][np.diff(o) > 0] - 1])
+        rows = np.unique(np.concatenate([edges, rng.choice(M, sample, replace=False)]))
+    ref, asum = oracle.grouped_gemm_w4a4(oa["codes"], oa["scales"], oa["tensor_scale"], off, n, k,
+                                         ow["codes"], ow["scales"], ow["tensor_scale"], rows=rows)
+    got = out.float().cpu().numpy()[rows].astype(np.float64)
+    err = np.abs(got - ref)
+    bound = 1e-3 * asum
+    if not strict:
+        bound = bound + 2.0 ** -8 * (1 + 2.0 ** -7) * np.abs(ref)
+    assert np.all(err <= bound), f"max err/bound {np.max(err / np.maximum(bound, 1e-300))}"
+
+
+def test_w4a4_gemm_moe_full_size():
+    _w4a4_check(inputs.zipf_counts(32, 16384, 1.1), 768, 2048, sample=256)
+
+
+def test_w4a4_gemm_forward_shape():
+    _w4a4_check(inputs.zipf_counts(64, 16384, 1.1), 2048, 768, sample=192)
+
+
+@pytest.mark.parametrize("counts,n,k", GEMM_EDGES)
+def test_w4a4_gemm_edges(counts, n, k):
+    _w4a4_check(counts, n, k, strict=False)
+
+
 def test_code_mismatch_random():
     rng = np.random.default_rng(3)
     B, per = 5, 4096
