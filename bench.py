@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=2)
     p.add_argument("--layers", type=int, default=LAYERS)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the rows measured outside the step (W4A4 GEMM, FP4 KV cache)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one 1 GiB device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -264,6 +266,8 @@ def main():
     if dom_cat == "gemm":
         roofline["algorithmic_flops_per_launch"] = gemm_flops
 
+    extras = None if args.no_extras else measure_extras(L, dev, stream, A, OFF, QG, QN, nl, first_hint)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(XR, XT, A, counts, first_hint)
@@ -293,10 +297,118 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "extras": extras,
         "mismatch": mism,
         "input_generation_s": round(t_gen, 1),
     }
     print(json.dumps(line), flush=True)
+
+
+def _time_phase(stream, fn, reps):
+    """Average event time (us) of `reps` back-to-back calls of fn on `stream`."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return 1e3 * e0.elapsed_time(e1) / reps
+
+
+def measure_extras(L, dev, stream, A, OFF, QG, QN, nl, first_hint):
+    """Rows measured outside the step, on the same device buffers:
+    * W4A4 grouped GEMM: each layer's activations quantized to NVFP4 (one tensor),
+      then the GEMM with the trainer's NVFP4 weights;
+    * FP4 KV cache with hints: one layer's K and V cache [32768 x 8 x 128] bf16,
+      rollout nearest + hints and trainer guided, per token-head blocks of 16."""
+    import ctypes as C
+
+    import torch
+
+    from fp4_quantization_precision_amd import inputs, ops
+    from fp4_quantization_precision_amd._lib import TQ_BF16
+
+    sp = C.c_void_p(stream.cuda_stream)
+    P = lambda t: C.c_void_p(t.data_ptr()) if t is not None else None
+    out = {}
+
+    # ---- W4A4 grouped GEMM ----
+    AQ = [ops.new_nvfp4((1,), TOKENS, COLS, dev) for _ in range(nl)]
+    OUT = torch.empty((TOKENS, ROWS), dtype=torch.bfloat16, device=dev)
+
+    def quant_a():
+        for l in range(nl):
+            st = L.tq_quantize(P(A[l]), TQ_BF16, 1, TOKENS, COLS, P(AQ[l].tensor_amax), P(AQ[l].codes),
+                               P(AQ[l].scales), P(AQ[l].tensor_scale), None, 0, sp)
+            assert st == 0
+
+    def w4a4():
+        for l in range(nl):
+            w = QG if l >= first_hint else QN
+            st = L.tq_grouped_gemm_w4a4(P(AQ[l].codes), P(AQ[l].scales), P(AQ[l].tensor_scale),
+                                        P(OFF), EXPERTS, TOKENS, ROWS, COLS, P(w.codes[l]),
+                                        P(w.scales[l]), P(w.tensor_scale[l]), P(OUT), sp)
+            assert st == 0
+
+    us_q = _time_phase(stream, quant_a, 3) / nl
+    us_g = _time_phase(stream, w4a4, 3) / nl
+    flops = 2.0 * TOKENS * COLS * ROWS
+    n_a = TOKENS * COLS
+    out["w4a4_quantize_activations"] = {
+        "kernel": "tq::amax_kernel + tq::quantize_kernel (tq_quantize, batch 1)",
+        "avg_us": round(us_q, 2), "GB/s": round(n_a * (2 + 2 + 0.5625) / us_q / 1e3, 1),
+        "note": "amax pass + quantize pass over [16384 x 768] bf16 per layer"}
+    out["w4a4_gemm"] = {
+        "kernel": "tq::grouped_gemm_nvfp4_kernel<true>", "avg_us": round(us_g, 2),
+        "TFLOP/s": round(flops / us_g / 1e6, 1),
+        "frac_bf16_mfma_peak": round(flops / us_g / 1e6 / BF16_MFMA_PEAK_TFLOPS, 4),
+        "shape": f"{EXPERTS} experts, {TOKENS} tokens, K {COLS}, N {ROWS}"}
+    del AQ, OUT
+
+    # ---- FP4 KV cache with hints ----
+    T, Hh, D = 32768, 8, 128
+    kr, kt, vr, vt, _ = inputs.kv_cache(T, Hh, D, device=dev)
+    R, n = T * Hh, T * Hh * D
+    H = torch.empty(2, ops.hint_words(n), dtype=torch.int32, device=dev)
+    QR = [ops.new_nvfp4((1,), R, D, dev) for _ in range(2)]
+    QT = [ops.new_nvfp4((1,), R, D, dev) for _ in range(2)]
+    xs_r, xs_t = (kr, vr), (kt, vt)
+    for i in range(2):  # trainer amax (given to the guided quantizer, as in the step)
+        assert L.tq_tensor_amax(P(xs_t[i]), TQ_BF16, 1, n, P(QT[i].tensor_amax), sp) == 0
+
+    def kv_hint():
+        for i in range(2):
+            st = L.tq_quantize(P(xs_r[i]), TQ_BF16, 1, R, D, P(QR[i].tensor_amax), P(QR[i].codes),
+                               P(QR[i].scales), P(QR[i].tensor_scale), P(H[i]), 0, sp)
+            assert st == 0
+
+    def kv_guided():
+        for i in range(2):
+            st = L.tq_quantize_guided(P(xs_t[i]), TQ_BF16, 1, R, D, P(QT[i].tensor_amax), P(H[i]),
+                                      P(QT[i].codes), P(QT[i].scales), P(QT[i].tensor_scale), 1, sp)
+            assert st == 0
+
+    us_h = _time_phase(stream, kv_hint, 5) / 2
+    us_gd = _time_phase(stream, kv_guided, 5) / 2
+    out["kv_quantize_hint"] = {
+        "kernel": "tq::amax_kernel + tq::quantize_kernel<true, 1>", "avg_us": round(us_h, 2),
+        "GB/s": round(n * (2 + 2 + 0.6875) / us_h / 1e3, 1),
+        "note": "per K or V tensor [32768 x 8 x 128]: amax pass + quantize with hints"}
+    out["kv_guided"] = {
+        "kernel": "tq::quantize_kernel<true, 2>", "avg_us": round(us_gd, 2),
+        "GB/s": round(n * 2.6875 / us_gd / 1e3, 1),
+        "frac_hbm_peak": round(n * 2.6875 / us_gd / 1e3 / HBM_PEAK_GBS, 4)}
+    cnt = torch.empty(2, 2, dtype=torch.int64, device=dev)
+    qn = ops.quantize(kt.view(1, R, D))
+    ops.code_mismatch(torch.cat([QR[0].codes.reshape(-1)] * 2),
+                      torch.cat([qn.codes.reshape(-1), QT[0].codes.reshape(-1)]), 2, n, counts=cnt)
+    c = cnt.cpu().numpy()
+    out["kv_mismatch_K"] = {"nearest_rate": float(c[0, 0] / n), "guided_rate": float(c[1, 0] / n),
+                            "nearest_adjacent_frac": float(c[0, 1] / max(c[0, 0], 1))}
+    return out
 
 
 # kernel name and source file of each timed category

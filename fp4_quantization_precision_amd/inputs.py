@@ -20,6 +20,10 @@ Workloads (sizes are the defaults of each function):
   workload.
 * ``activations`` - [32768 x 4096] bf16 Student-t(4) values with 8 fixed outlier
   channels x50; training copy perturbed by uniform relative noise of +-2^-8.
+* ``kv_cache`` - one layer's K and V cache [32768 tokens x 8 heads x 128] bf16,
+  K with 4 outlier channels per head x20, V ~ N(0,1); training copies perturbed by
+  uniform relative noise of +-2^-8.  Quantized per token-head (blocks of 16 along
+  head_dim).
 * ``transpose_source`` - [8192 x 8192] bf16 ~ N(0,1).
 * ``grouped_gemm_inputs`` - 32 experts with Zipf(1.1) token counts summing to
   16384; A = bf16 N(0,1) [tokens x 2048]; expert weights bf16 N(0,0.02)
@@ -35,6 +39,7 @@ __all__ = [
     "tiny_roundtrip",
     "moe_expert_weights_layer",
     "activations",
+    "kv_cache",
     "transpose_source",
     "zipf_counts",
     "group_offsets",
@@ -103,6 +108,32 @@ def activations(tokens: int = 32768, hidden: int = 4096, device="cpu", seed: int
     u = (torch.rand(shape, generator=g, device=device, dtype=torch.float32) * 2.0 - 1.0) * 2.0 ** -8
     xt = (xr.float() * (1.0 + u)).to(torch.bfloat16)
     return xr.contiguous(), xt.contiguous(), ch.cpu()
+
+
+def kv_cache(tokens: int = 32768, heads: int = 8, head_dim: int = 128, device="cpu", seed: int = 6,
+             outlier_channels: int = 4, outlier_scale: float = 20.0):
+    """One layer's K and V cache [tokens][heads][head_dim] bf16, rollout and training
+    copies.  K ~ N(0, 1) with `outlier_channels` fixed head_dim channels per head
+    scaled x`outlier_scale` (keys concentrate magnitude in a few channels); V ~ N(0, 1).
+    Training copies are bf16(X_r * (1 + u)), u ~ U(-2^-8, 2^-8), as for activations.
+    Returns (k_r, k_t, v_r, v_t, outlier channel ids [heads, outlier_channels])."""
+    g = _gen(seed, device)
+    shape = (tokens, heads, head_dim)
+    kr = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    gc = _gen(seed + 17, "cpu")
+    ch = torch.stack([torch.randperm(head_dim, generator=gc)[:outlier_channels] for _ in range(heads)])
+    for h in range(heads):
+        kr[:, h, ch[h].to(device)] *= outlier_scale
+    kr = kr.to(torch.bfloat16)
+    vr = torch.randn(shape, generator=g, device=device, dtype=torch.float32).to(torch.bfloat16)
+
+    def trainer_copy(x):
+        u = (torch.rand(shape, generator=g, device=device, dtype=torch.float32) * 2.0 - 1.0) * 2.0 ** -8
+        return (x.float() * (1.0 + u)).to(torch.bfloat16)
+
+    kt = trainer_copy(kr)
+    vt = trainer_copy(vr)
+    return kr.contiguous(), kt.contiguous(), vr.contiguous(), vt.contiguous(), ch
 
 
 def transpose_source(rows: int = 8192, cols: int = 8192, device="cpu", seed: int = 4):

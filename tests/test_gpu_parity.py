@@ -319,6 +319,49 @@ def test_activations_full_size():
     print(f"\nactivations: mismatch rate nearest {c[0, 0] / n:.3e} -> guided {c[1, 0] / n:.3e}")
 
 
+@pytest.mark.parametrize("which", ["K", "V"])
+def test_kv_cache_full_size(which):
+    """FP4 KV cache with hints: one layer's K (or V) cache [32768 x 8 x 128] quantized
+    per token-head (blocks of 16 along head_dim, one tensor scale), rollout nearest +
+    hints, trainer guided; sampled token-heads bit-exact against the oracle, full
+    mismatch counts checked against the oracle's on the same rows."""
+    T, Hh, D = 32768, 8, 128
+    kr, kt, vr, vt, _ = inputs.kv_cache(T, Hh, D, device=DEV)
+    xr, xt = (kr, kt) if which == "K" else (vr, vt)
+    R = T * Hh
+    n = xr.numel()
+    hints = torch.zeros(ops.hint_words(n), dtype=torch.int32, device=DEV)
+    qr = ops.quantize(xr.view(1, R, D), hints_out=hints)
+    qg = ops.quantize_guided(xt.view(1, R, D), hints)
+    qn = ops.quantize(xt.view(1, R, D))
+    cnt = ops.code_mismatch(torch.cat([qr.codes.reshape(-1)] * 2),
+                            torch.cat([qn.codes.reshape(-1), qg.codes.reshape(-1)]), 2, n)
+    torch.cuda.synchronize()
+    xr_c, xt_c = xr.reshape(R, D).cpu(), xt.reshape(R, D).cpu()
+    am_r = oracle.tensor_amax(xr_c, 1, n)
+    am_t = oracle.tensor_amax(xt_c, 1, n)
+    assert npu8(qr.tensor_amax)[0] == am_r[0] and npu8(qg.tensor_amax)[0] == am_t[0]
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([[0, 1, R - 1], rng.choice(R, 509, replace=False)]))
+    o_r = oracle.quantize(xr_c[rows], 1, rows.size, D, amax=am_r)
+    o_h = oracle.extract_hint(o_r["codes"], rows.size * D)
+    o_g = oracle.quantize_guided(xt_c[rows], 1, rows.size, D, o_h, amax=am_t)
+    o_n = oracle.quantize(xt_c[rows], 1, rows.size, D, amax=am_t)
+    codes_r = npu8(qr.codes).reshape(R, D // 2)[rows].reshape(-1)
+    codes_g = npu8(qg.codes).reshape(R, D // 2)[rows].reshape(-1)
+    codes_n = npu8(qn.codes).reshape(R, D // 2)[rows].reshape(-1)
+    assert np.array_equal(codes_r, o_r["codes"])
+    assert np.array_equal(npu8(qr.scales).reshape(R, D // 16)[rows].reshape(-1), o_r["scales"])
+    assert np.array_equal(hints_np(hints).reshape(R, D // 32)[rows].reshape(-1), o_h)
+    assert np.array_equal(codes_g, o_g["codes"])
+    assert np.array_equal(npu8(qg.scales).reshape(R, D // 16)[rows].reshape(-1), o_g["scales"])
+    assert np.array_equal(codes_n, o_n["codes"])
+    c = cnt.cpu().numpy()
+    assert c[1, 0] <= c[0, 0]
+    print(f"\nKV cache {which}: mismatch rate nearest {c[0, 0] / n:.3e} "
+          f"(adjacent {c[0, 1] / max(c[0, 0], 1):.3f}) -> guided {c[1, 0] / n:.3e}")
+
+
 # ----------------------------------------------------------------------------------
 # Transpose-requantize with stochastic rounding
 # ----------------------------------------------------------------------------------

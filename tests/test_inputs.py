@@ -55,3 +55,17 @@ def test_random_nvfp4():
     c, s, t = inputs.random_nvfp4(2, 32, 64, zero_block_frac=0.2)
     assert c.shape == (2, 32, 32) and s.shape == (2, 32, 4) and t.shape == (2,)
     assert s.max().item() <= 0x7E and (s == 0).any()
+
+
+def test_kv_cache_small():
+    kr, kt, vr, vt, ch = inputs.kv_cache(64, 2, 32, outlier_channels=2)
+    assert kr.shape == (64, 2, 32) and kr.dtype == torch.bfloat16
+    assert ch.shape == (2, 2)
+    for h in range(2):
+        big = kr[:, h, ch[h]].float().abs().mean()
+        rest = kr[:, h].float().abs().mean()
+        assert big > 5 * rest
+    rel = ((kt.float() - kr.float()).abs() / kr.float().abs().clamp_min(1e-30)).max()
+    assert rel <= 2.0 ** -8 + 2.0 ** -8  # noise bound plus one bf16 rounding
+    kr2, _, vr2, _, _ = inputs.kv_cache(64, 2, 32, outlier_channels=2)
+    assert torch.equal(kr, kr2) and torch.equal(vr, vr2)
