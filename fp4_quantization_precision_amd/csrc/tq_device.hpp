@@ -50,24 +50,6 @@ __device__ __forceinline__ uint32_t e4m3_encode(float d)
 // E2M1 element codes
 // ---------------------------------------------------------------------------
 
-// Nearest magnitude index for a >= 0 with ties to the even index, saturating at
-// 6: count the decision thresholds passed.  Midpoints that tie upward to an even
-// index use >=, those that tie downward use >.
-__device__ __forceinline__ uint32_t e2m1_nearest(float a)
-{
-    return (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-           (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-           (uint32_t)(a > 5.0f);
-}
-
-// Largest index lo with G[lo] <= a (a >= 0).
-__device__ __forceinline__ uint32_t e2m1_floor(float a)
-{
-    return (uint32_t)(a >= 0.5f) + (uint32_t)(a >= 1.0f) + (uint32_t)(a >= 1.5f) +
-           (uint32_t)(a >= 2.0f) + (uint32_t)(a >= 3.0f) + (uint32_t)(a >= 4.0f) +
-           (uint32_t)(a >= 6.0f);
-}
-
 // G[m] as binary32.
 __device__ __forceinline__ float e2m1_value(uint32_t m)
 {
@@ -76,59 +58,25 @@ __device__ __forceinline__ float e2m1_value(uint32_t m)
     return m >= 2 ? v : (m == 1 ? 0.5f : 0.0f);
 }
 
-// Smallest index hi with G[hi] >= a, for 0 <= a <= 6.
-__device__ __forceinline__ uint32_t e2m1_ceil(float a)
-{
-    return (uint32_t)(a > 0.0f) + (uint32_t)(a > 0.5f) + (uint32_t)(a > 1.0f) +
-           (uint32_t)(a > 1.5f) + (uint32_t)(a > 2.0f) + (uint32_t)(a > 3.0f) +
-           (uint32_t)(a > 4.0f);
-}
-
-// TRACE guided choice ([TRACE] "TRACE" explainer, paragraph after the rounding
-// analogy): of the two grid points around a, take the one whose mantissa bit
-// equals the rollout's hint bit h; grid points and a >= 6 are fixed.
-__device__ __forceinline__ uint32_t e2m1_guided(float a, uint32_t h)
-{
-    if (a >= 6.0f)
-        return 7u;
-    uint32_t lo = e2m1_floor(a);
-    uint32_t hi = e2m1_ceil(a);
-    if (lo == hi)
-        return lo;
-    return ((lo & 1u) == h) ? lo : hi;
-}
-
-// Stochastic rounding between the two grid points around a with random byte k
-// ([TML] forward/backward-mismatch paragraph, the 2.25 example): up iff
-// k < 256 * (a - G[lo]) / (G[lo+1] - G[lo]).  The subtraction is exact
-// (Sterbenz, or G[lo] = 0) and the division is by a power of two, so the
-// threshold is exact and so is the comparison.
-__device__ __forceinline__ uint32_t e2m1_sr(float a, uint32_t k)
-{
-    if (a >= 6.0f)
-        return 7u;
-    uint32_t lo = e2m1_floor(a);
-    float glo = e2m1_value(lo);
-    // 256 / (G[lo+1] - G[lo]): 512 below 2, 256 in [2, 4), 128 in [4, 6)
-    float inv = lo < 4 ? 512.0f : (lo < 6 ? 256.0f : 128.0f);
-    float t = (a - glo) * inv;
-    return ((float)k < t) ? lo + 1u : lo;
-}
-
-// Sign and magnitude into a 4-bit code; zero is always +0.
-__device__ __forceinline__ uint32_t e2m1_code(float y, uint32_t m)
-{
-    return m | ((y < 0.0f && m != 0u) ? 8u : 0u);
-}
+// The rounding rules the kernels implement, for a = |y| on the grid G above:
+//  nearest: the grid point nearest to a, ties to the even index, a > 5 -> 6;
+//  guided ([TRACE] "TRACE" explainer, paragraph after the rounding analogy):
+//    a >= 6 -> 6; a on the grid keeps its index lo; otherwise the one of lo and
+//    lo + 1 whose mantissa bit (index & 1) equals the hint bit;
+//  stochastic ([TML] forward/backward-mismatch paragraph, the 2.25 example):
+//    a >= 6 -> 6; otherwise lo + 1 iff k < 256 (a - G[lo]) / (G[lo+1] - G[lo])
+//    for the element's random byte k (exact: the subtraction is exact and the
+//    divisor a power of two).
+// A code is the magnitude index plus 8 for y < 0; zero is always +0.
 
 // ---------------------------------------------------------------------------
-// Fast forms used by the kernels.  Each one is an exact re-expression of the
+// Packed forms used by the kernels.  Each one is an exact re-expression of the
 // rules above (checked bit for bit against the CPU oracle by the GPU tests).
 // ---------------------------------------------------------------------------
 
 // Eight nearest codes packed into one dword (element i in nibble i).  gfx950's
 // v_cvt_scalef32_pk_fp4_f32 with scale 1 rounds to nearest even and saturates at
-// 6 exactly like e2m1_nearest/e2m1_code for every finite binary32 input, except
+// 6 exactly like the nearest rule for every finite binary32 input, except
 // that it keeps the sign of a value that rounds to zero; the mask below turns
 // every -0 nibble (code 8) into +0.
 __device__ __forceinline__ uint32_t clear_negative_zero(uint32_t w)
@@ -146,6 +94,28 @@ __device__ __forceinline__ uint32_t pack8_nearest(const float y[8])
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], 1.0f, 2);
     w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], 1.0f, 3);
     return clear_negative_zero(w);
+}
+
+// Byte SEL of `w` <- the two floor codes of (a, b): v_cvt_scalef32_sr_pk_fp4_f32
+// with a zero seed and unit scale truncates each value to the grid toward zero
+// (sign kept) and leaves the other three bytes of the destination unchanged.
+// Written in asm because the compiler does not treat this destination as tied
+// to its previous value; a byte-selected write needs one wait state before the
+// register is read again (the s_nop the compiler puts after such writes).
+template <int SEL>
+__device__ __forceinline__ uint32_t floor_pk_fp4(uint32_t w, float a, float b)
+{
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 v = {a, b};
+    if (SEL == 0)
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, 0, 1.0" : "+v"(w) : "v"(v));
+    else if (SEL == 1)
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, 0, 1.0 op_sel:[0,0,1,0]\n\ts_nop 0" : "+v"(w) : "v"(v));
+    else if (SEL == 2)
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, 0, 1.0 op_sel:[0,0,0,1]\n\ts_nop 0" : "+v"(w) : "v"(v));
+    else
+        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, 0, 1.0 op_sel:[0,0,1,1]\n\ts_nop 0" : "+v"(w) : "v"(v));
+    return w;
 }
 
 // Mantissa bits (m & 1) of eight packed codes, gathered into bits 0..7.
@@ -175,41 +145,41 @@ __device__ __forceinline__ uint32_t pack_hi16(float a, float b)
     return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
 }
 
-// Floor grid index of a >= 0 from its bits: above 1 the grid is a binary float
-// with one mantissa bit, so lo = (bits >> 22) - 252 (the exponent and the top
-// mantissa bit); [0.5, 1) gives 1 and [0, 0.5) gives 0; clamped to 7.
-__device__ __forceinline__ uint32_t e2m1_floor_bits(float a)
+// Bits 0..7 of h spread to bit 0 of nibbles 0..7 (the inverse of parity8).
+__device__ __forceinline__ uint32_t spread8(uint32_t h)
 {
-    const int b = (int)(__float_as_uint(a) >> 22) - 252;
-    const int lo = b > (int)(a >= 0.5f) ? b : (int)(a >= 0.5f);
-    return (uint32_t)(lo < 7 ? lo : 7);
+    uint32_t x = h & 0xFFu;
+    x = (x | (x << 12)) & 0x000F000Fu;
+    x = (x | (x << 6)) & 0x03030303u;
+    x = (x | (x << 3)) & 0x11111111u;
+    return x;
 }
 
-// e2m1_guided without compare chains: a is on the grid iff the bits below the
-// grid's resolution are zero (22 mantissa bits above 1, 23 in [0.5, 1), all of
-// them below 0.5).  Off the grid the bracket is (lo, lo+1) and the hint picks
-// the end with its parity: lo + ((lo ^ h) & 1).  a >= 6 gives 7.
-__device__ __forceinline__ uint32_t e2m1_guided_bits(float a, uint32_t h)
+// Eight guided codes packed into one dword (element i in nibble i), hint bit i
+// in bit i of h: the guided rule on values clamped to [-6, 6] (which
+// leaves every decision unchanged and makes a >= 6 an on-grid 6).  Floor codes
+// come from the hardware truncation; off the grid the code steps up by one
+// exactly when the floor's mantissa bit differs from the hint.
+__device__ __forceinline__ uint32_t pack8_guided(const float y[8], uint32_t h)
 {
-    const uint32_t bits = __float_as_uint(a);
-    const uint32_t lo = e2m1_floor_bits(a);
-    const uint32_t mask = a >= 1.0f ? 0x3FFFFFu : (a >= 0.5f ? 0x7FFFFFu : 0x7FFFFFFFu);
-    const bool on_grid = (bits & mask) == 0u;
-    const uint32_t m = on_grid ? lo : lo + ((lo ^ h) & 1u);
-    return m < 7u ? m : 7u;
-}
-
-// e2m1_sr without compare chains: up iff k < 256 (a - G[lo]) / D with
-// D = G[lo+1] - G[lo], i.e. iff G[lo] + k * (D / 256) < a, where G[lo] (at most
-// two significant bits) plus k * D / 256 (at most eight) is exact in binary32.
-// D / 256 is 2^-9 below 2, 2^-8 in [2, 4) and 2^-7 from 4; a >= 6 gives 7.
-__device__ __forceinline__ uint32_t e2m1_sr_bits(float a, float k)
-{
-    const uint32_t lo = e2m1_floor_bits(a);
-    const float glo = lo >= 2u ? __uint_as_float((lo + 252u) << 22) : (lo == 1u ? 0.5f : 0.0f);
-    const float q = lo < 4u ? 0x1p-9f : (lo < 6u ? 0x1p-8f : 0x1p-7f);
-    const uint32_t m = lo + ((glo + k * q < a) ? 1u : 0u);
-    return m < 7u ? m : 7u;
+    float yc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        yc[i] = __builtin_amdgcn_fmed3f(y[i], -6.0f, 6.0f);
+    uint32_t P = 0;
+    P = floor_pk_fp4<0>(P, yc[0], yc[1]);
+    P = floor_pk_fp4<1>(P, yc[2], yc[3]);
+    P = floor_pk_fp4<2>(P, yc[4], yc[5]);
+    P = floor_pk_fp4<3>(P, yc[6], yc[7]);
+    const tq_f32x2 g0 = fp4x2_to_f32<0>(P), g1 = fp4x2_to_f32<1>(P);
+    const tq_f32x2 g2 = fp4x2_to_f32<2>(P), g3 = fp4x2_to_f32<3>(P);
+    const float g[8] = {g0[0], g0[1], g1[0], g1[1], g2[0], g2[1], g3[0], g3[1]};
+    uint32_t off = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        off |= (fabsf(g[i]) != fabsf(yc[i])) ? (1u << (4 * i)) : 0u;
+    const uint32_t up = (P ^ spread8(h)) & off;  // bit 0 of each nibble
+    return clear_negative_zero(P + up);
 }
 
 // ---------------------------------------------------------------------------

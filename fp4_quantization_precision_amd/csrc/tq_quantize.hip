@@ -242,14 +242,8 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
                 for (int i = 0; i < 16; ++i)
                     y[i] = v[i] * r_b;
                 if (MODE == MODE_GUIDED) {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const uint32_t c = e2m1_code(y[i], e2m1_guided_bits(fabsf(y[i]), (hin >> i) & 1u));
-                        if (i < 8)
-                            lo |= c << (4 * i);
-                        else
-                            hi |= c << (4 * (i - 8));
-                    }
+                    lo = pack8_guided(y, hin);
+                    hi = pack8_guided(y + 8, hin >> 8);
                 } else {
                     lo = pack8_nearest(y);
                     hi = pack8_nearest(y + 8);

@@ -52,28 +52,6 @@ __device__ __forceinline__ float sr_step(float glo)
     return __int_as_float(e > 0x3B000000 ? e : 0x3B000000);
 }
 
-// Byte SEL of `w` <- the two floor codes of (a, b): v_cvt_scalef32_sr_pk_fp4_f32
-// with a zero seed and unit scale truncates each value to the grid toward zero
-// (sign kept) and leaves the other three bytes of the destination unchanged.
-// Written in asm because the compiler does not treat this destination as tied
-// to its previous value; a byte-selected write needs one wait state before the
-// register is read again (the s_nop the compiler puts after such writes).
-template <int SEL>
-__device__ __forceinline__ uint32_t floor_pk_fp4(uint32_t w, float a, float b)
-{
-    typedef float f2 __attribute__((ext_vector_type(2)));
-    const f2 v = {a, b};
-    if (SEL == 0)
-        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, 0, 1.0" : "+v"(w) : "v"(v));
-    else if (SEL == 1)
-        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, 0, 1.0 op_sel:[0,0,1,0]\n\ts_nop 0" : "+v"(w) : "v"(v));
-    else if (SEL == 2)
-        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, 0, 1.0 op_sel:[0,0,0,1]\n\ts_nop 0" : "+v"(w) : "v"(v));
-    else
-        asm("v_cvt_scalef32_sr_pk_fp4_f32 %0, %1, 0, 1.0 op_sel:[0,0,1,1]\n\ts_nop 0" : "+v"(w) : "v"(v));
-    return w;
-}
-
 // Stochastic rounding of eight clamped values (|yc| <= 6) with their random
 // bytes k[0..7]: floor codes from the hardware truncation, plus one where the
 // random byte falls below the distance to the floor point.
