@@ -74,6 +74,8 @@ def lib():
         L.tqo_sr_index.restype = i32
         L.tqo_requant_transpose_sr.argtypes = [p, p, p, i64, i64, i64, C.c_uint64, p, p, p]
         L.tqo_grouped_gemm.argtypes = [p, p, C.c_int32, i64, i64, p, p, p, p, i64, p, p]
+        L.tqo_quantize_tile16.argtypes = [p, i32, i64, i64, i64, i32, p, p, p, p]
+        L.tqo_transpose_tile16.argtypes = [p, p, p, i64, i64, i64, p, p, p]
         L.tqo_grouped_gemm_w4a4.argtypes = [p, p, p, p, C.c_int32, i64, i64, p, p, p, p, i64, p, p]
         L.tqo_code_mismatch.argtypes = [p, p, i64, i64, p]
         L.tqo_e4m3_encode_array.argtypes = [p, i64, p]
@@ -249,6 +251,30 @@ def grouped_gemm(a, group_offsets, n: int, k: int, w_codes, w_scales, w_tensor_s
     lib().tqo_grouped_gemm(_ptr(A), _ptr(off), off.size - 1, n, k, _ptr(wc), _ptr(ws), _ptr(wt),
                            _ptr(rows), rows.size, _ptr(ref), _ptr(asum))
     return ref, asum
+
+
+def quantize_tile16(x, batch: int, rows: int, cols: int, amax=None):
+    """16x16-tile quantizer: codes [batch*rows*cols/2], scales [batch*(rows/16)*(cols/16)]."""
+    a, dt = _x_and_dtype(x)
+    n = batch * rows * cols
+    codes = np.zeros(n // 2, np.uint8)
+    scales = np.zeros(batch * (rows // 16) * (cols // 16), np.uint8)
+    ts = np.zeros(batch, np.float32)
+    am = np.zeros(batch, np.float32) if amax is None else np.ascontiguousarray(amax, np.float32).copy()
+    lib().tqo_quantize_tile16(_ptr(a), dt, batch, rows, cols, int(amax is not None), _ptr(am),
+                              _ptr(codes), _ptr(scales), _ptr(ts))
+    return {"codes": codes, "scales": scales, "tensor_scale": ts, "tensor_amax": am}
+
+
+def transpose_tile16(codes, scales, tensor_scale, batch: int, rows: int, cols: int):
+    c, s = _np(codes, np.uint8), _np(scales, np.uint8)
+    ts = _np(tensor_scale, np.float32)
+    ct = np.zeros(c.size, np.uint8)
+    st = np.zeros(s.size, np.uint8)
+    tst = np.zeros(batch, np.float32)
+    lib().tqo_transpose_tile16(_ptr(c), _ptr(s), _ptr(ts), batch, rows, cols, _ptr(ct), _ptr(st),
+                               _ptr(tst))
+    return {"codes": ct, "scales": st, "tensor_scale": tst}
 
 
 def grouped_gemm_w4a4(a_codes, a_scales, a_tensor_scale, group_offsets, n: int, k: int, w_codes,

@@ -557,6 +557,89 @@ void tqo_grouped_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales,
 }
 
 /* ------------------------------------------------------------------------ */
+/* 16x16-tile scaling                                                        */
+/* ------------------------------------------------------------------------ */
+
+/* [TML] forward/backward-mismatch paragraph: the 16x16-tile alternative gives
+ * one scale to a tile of 16 rows x 16 columns (256 values), so a transpose
+ * keeps every value's group; a single large value can zero the rest of its
+ * tile.  Steps as Q, with the block maximum taken over the tile: s_t =
+ * A_T/2688; per tile d = fl(fl(A_tile/6)/s_t) -> E4M3 e; S = fl(dec(e) s_t),
+ * r = fl(1/S); per element the nearest E2M1 code of fl(x r).
+ * codes [batch][rows][cols/2] as Q; scales [batch][rows/16][cols/16]. */
+void tqo_quantize_tile16(const void *x, int dtype, int64_t batch, int64_t rows, int64_t cols,
+                         int amax_given, float *tensor_amax, uint8_t *codes, uint8_t *scales,
+                         float *tensor_scale)
+{
+    const int64_t per_tensor = rows * cols;
+    const int64_t tr = rows / 16, tc = cols / 16;
+    for (int64_t b = 0; b < batch; ++b) {
+        float A_T;
+        if (amax_given) {
+            A_T = tensor_amax[b];
+        } else {
+            A_T = 0.0f;
+            for (int64_t i = 0; i < per_tensor; ++i) {
+                float v = fabsf(load_x(x, dtype, b * per_tensor + i));
+                if (v > A_T)
+                    A_T = v;
+            }
+            tensor_amax[b] = A_T;
+        }
+        float s_t = (A_T == 0.0f) ? 0.0f : A_T / 2688.0f;
+        tensor_scale[b] = s_t;
+        for (int64_t ti = 0; ti < tr; ++ti) {
+            for (int64_t tj = 0; tj < tc; ++tj) {
+                float A = 0.0f;
+                for (int u = 0; u < 16; ++u)
+                    for (int v = 0; v < 16; ++v) {
+                        float a = fabsf(load_x(x, dtype, b * per_tensor + (16 * ti + u) * cols + 16 * tj + v));
+                        if (a > A)
+                            A = a;
+                    }
+                uint8_t e = 0;
+                if (s_t != 0.0f)
+                    e = tqo_e4m3_encode((A / 6.0f) / s_t);
+                scales[(b * tr + ti) * tc + tj] = e;
+                float dec = (float)tqo_e4m3_value(e);
+                float r = dec == 0.0f ? 0.0f : 1.0f / (dec * s_t);
+                for (int u = 0; u < 16; ++u)
+                    for (int v = 0; v < 16; ++v) {
+                        int64_t i = b * per_tensor + (16 * ti + u) * cols + 16 * tj + v;
+                        int code = 0;
+                        if (dec != 0.0f) {
+                            float y = load_x(x, dtype, i) * r;
+                            int m = tqo_e2m1_nearest(fabsf(y));
+                            code = ((y < 0.0f && m != 0) ? 8 : 0) + m;
+                        }
+                        put_code(codes, i, code);
+                    }
+            }
+        }
+    }
+}
+
+/* Transpose of a 16x16-tile NVFP4 tensor: every value keeps its tile, so codes
+ * and tile scales are moved, nothing is requantized.  codes_t [batch][cols][rows/2],
+ * scales_t [batch][cols/16][rows/16], tensor scale copied. */
+void tqo_transpose_tile16(const uint8_t *codes, const uint8_t *scales, const float *tensor_scale,
+                          int64_t batch, int64_t rows, int64_t cols, uint8_t *codes_t,
+                          uint8_t *scales_t, float *tensor_scale_t)
+{
+    const int64_t tr = rows / 16, tc = cols / 16;
+    for (int64_t b = 0; b < batch; ++b) {
+        tensor_scale_t[b] = tensor_scale[b];
+        for (int64_t r = 0; r < rows; ++r)
+            for (int64_t c = 0; c < cols; ++c)
+                put_code(codes_t, (b * cols + c) * rows + r,
+                         tqo_get_code(codes, (b * rows + r) * cols + c));
+        for (int64_t ti = 0; ti < tr; ++ti)
+            for (int64_t tj = 0; tj < tc; ++tj)
+                scales_t[(b * tc + tj) * tr + ti] = scales[(b * tr + ti) * tc + tj];
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Mismatch statistics                                                       */
 /* ------------------------------------------------------------------------ */
 

@@ -706,6 +706,63 @@ def test_w4a4_gemm_reduces_to_w4a16(orc):
 
 
 # ----------------------------------------------------------------------------------
+# 16x16-tile scaling
+# ----------------------------------------------------------------------------------
+
+def test_tile16_transpose_invariance(orc):
+    """A transpose keeps every value's 16x16 tile, so quantizing the transposed
+    tensor equals transposing the quantized one, bit for bit."""
+    rng = np.random.default_rng(41)
+    R, Cc = 48, 80
+    x = rng.standard_normal((R, Cc)).astype(np.float32)
+    x[rng.random(x.shape) < 0.01] *= 30
+    q = orc.quantize_tile16(x, 1, R, Cc)
+    t = orc.transpose_tile16(q["codes"], q["scales"], q["tensor_scale"], 1, R, Cc)
+    qt = orc.quantize_tile16(np.ascontiguousarray(x.T), 1, Cc, R)
+    assert np.array_equal(t["codes"], qt["codes"])
+    assert np.array_equal(t["scales"], qt["scales"])
+    assert np.array_equal(t["tensor_scale"], qt["tensor_scale"])
+    # and the transpose is an involution
+    tt = orc.transpose_tile16(t["codes"], t["scales"], t["tensor_scale"], 1, Cc, R)
+    assert np.array_equal(tt["codes"], q["codes"]) and np.array_equal(tt["scales"], q["scales"])
+
+
+def test_tile16_reduces_to_block16_when_every_block_holds_the_tile_max(orc):
+    """If each row block of 16 inside a tile already contains the tile's largest
+    magnitude, tile and block scales coincide and so do all codes (Q is pinned)."""
+    rng = np.random.default_rng(43)
+    R, Cc = 32, 64
+    x = rng.uniform(-1, 1, (R, Cc)).astype(np.float32)
+    for ti in range(R // 16):
+        for tj in range(Cc // 16):
+            m = np.float32(rng.uniform(1.5, 40.0))
+            for u in range(16):
+                x[16 * ti + u, 16 * tj + rng.integers(16)] = m if rng.random() < 0.5 else -m
+    q16 = orc.quantize_tile16(x, 1, R, Cc)
+    qb = orc.quantize(x, 1, R, Cc)
+    assert np.array_equal(q16["codes"], qb["codes"])
+    tile_scales = q16["scales"].reshape(R // 16, Cc // 16)
+    assert np.array_equal(np.repeat(tile_scales, 16, axis=0), qb["scales"].reshape(R, Cc // 16))
+
+
+def test_tile16_one_large_value_zeros_its_tile(orc):
+    """[TML] forward/backward-mismatch paragraph: one large value zeros the rest of
+    its tile.  Closed form: with 1000 among 255 ones, s_t = 1000/2688 and the tile
+    scale is E4M3 448 (d = (1000/6)/s_t = 448), so a one scales to
+    y = 1/(448 s_t) = 0.006 -> code 0 while 1000 -> 6 (code 7); per-16 blocks zero
+    only the 15 ones that share the large value's row block."""
+    x = np.ones((16, 16), np.float32)
+    x[0, 0] = 1000.0
+    q16 = orc.quantize_tile16(x, 1, 16, 16)
+    codes = unpack(q16["codes"], 256)
+    assert q16["scales"][0] == 0x7E
+    assert codes[0] == 7 and (codes[1:] == 0).all()
+    qb = orc.quantize(x, 1, 16, 16)
+    cb = unpack(qb["codes"], 256)
+    assert cb[0] == 7 and (cb[1:16] == 0).all() and (cb[16:] != 0).all()
+
+
+# ----------------------------------------------------------------------------------
 # Mismatch statistics
 # ----------------------------------------------------------------------------------
 
