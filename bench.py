@@ -323,7 +323,9 @@ def measure_extras(L, dev, stream, A, OFF, QG, QN, nl, first_hint):
     * W4A4 grouped GEMM: each layer's activations quantized to NVFP4 (one tensor),
       then the GEMM with the trainer's NVFP4 weights;
     * FP4 KV cache with hints: one layer's K and V cache [32768 x 8 x 128] bf16,
-      rollout nearest + hints and trainer guided, per token-head blocks of 16."""
+      rollout nearest + hints and trainer guided, per token-head blocks of 16;
+    * 16x16-tile scaling: quantize and exact transpose of the activations
+      workload [32768 x 4096] bf16, and the share of zero codes against block-16."""
     import ctypes as C
 
     import torch
@@ -401,6 +403,41 @@ def measure_extras(L, dev, stream, A, OFF, QG, QN, nl, first_hint):
         "kernel": "tq::quantize_kernel<true, 2>", "avg_us": round(us_gd, 2),
         "GB/s": round(n * 2.6875 / us_gd / 1e3, 1),
         "frac_hbm_peak": round(n * 2.6875 / us_gd / 1e3 / HBM_PEAK_GBS, 4)}
+    # ---- 16x16-tile scaling on the activations workload ----
+    T2, Hd = 32768, 4096
+    xa, _, _ = inputs.activations(T2, Hd, device=dev)
+    n2 = T2 * Hd
+    q16 = ops.quantize_tile16(xa)
+    qt16 = ops.transpose_tile16(q16, 1, T2, Hd)
+
+    def tile_quant():
+        assert L.tq_quantize_tile16(P(xa), TQ_BF16, 1, T2, Hd, P(q16.tensor_amax), P(q16.codes),
+                                    P(q16.scales), P(q16.tensor_scale), 1, sp) == 0
+
+    def tile_transpose():
+        assert L.tq_transpose_tile16(P(q16.codes), P(q16.scales), P(q16.tensor_scale), 1, T2, Hd,
+                                     P(qt16.codes), P(qt16.scales), P(qt16.tensor_scale), sp) == 0
+
+    us_tq = _time_phase(stream, tile_quant, 5)
+    us_tt = _time_phase(stream, tile_transpose, 5)
+    b_tq = n2 * (2 + 0.5 + 1 / 256)
+    b_tt = n2 * 2 * (0.5 + 1 / 256)
+    qb = ops.quantize(xa)
+    zero16 = ((q16.codes & 0x07) == 0).sum() + ((q16.codes & 0x70) == 0).sum()
+    zerob = ((qb.codes & 0x07) == 0).sum() + ((qb.codes & 0x70) == 0).sum()
+    nz = (xa != 0).sum()
+    out["tile16_quantize"] = {
+        "kernel": "tq::quantize_tile16_kernel<true>", "avg_us": round(us_tq, 2),
+        "GB/s": round(b_tq / us_tq / 1e3, 1), "frac_hbm_peak": round(b_tq / us_tq / 1e3 / HBM_PEAK_GBS, 4),
+        "workload": f"activations [{T2} x {Hd}] bf16, amax given"}
+    out["tile16_transpose"] = {
+        "kernel": "tq::transpose_tile16_kernel", "avg_us": round(us_tt, 2),
+        "GB/s": round(b_tt / us_tt / 1e3, 1), "frac_hbm_peak": round(b_tt / us_tt / 1e3 / HBM_PEAK_GBS, 4)}
+    out["tile16_vs_block16_zeroed"] = {
+        "tile16_zero_codes_frac": float(zero16) / n2, "block16_zero_codes_frac": float(zerob) / n2,
+        "nonzero_inputs_frac": float(nz) / n2}
+    del xa, q16, qt16, qb
+
     cnt = torch.empty(2, 2, dtype=torch.int64, device=dev)
     qn = ops.quantize(kt.view(1, R, D))
     ops.code_mismatch(torch.cat([QR[0].codes.reshape(-1)] * 2),

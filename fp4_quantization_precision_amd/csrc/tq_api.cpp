@@ -186,6 +186,65 @@ TQ_API tq_status tq_grouped_gemm_nvfp4(const uint16_t* a, const int32_t* group_o
     return launch_status();
 }
 
+TQ_API tq_status tq_quantize_tile16(const void* x, int32_t dtype, int64_t batch, int64_t rows,
+                                    int64_t cols, float* tensor_amax, uint8_t* codes,
+                                    uint8_t* scales, float* tensor_scale, uint32_t flags,
+                                    void* stream)
+{
+    if (dtype != TQ_F32 && dtype != TQ_BF16)
+        return TQ_ERR_DTYPE;
+    if (flags & ~static_cast<uint32_t>(TQ_AMAX_GIVEN))
+        return TQ_ERR_FLAGS;
+    int64_t n;
+    if (!product(batch, rows, cols, &n) || rows % 16 != 0 || cols % 16 != 0)
+        return TQ_ERR_SHAPE;
+    if (batch == 0)
+        return TQ_OK;
+    if (!tensor_amax || !tensor_scale)
+        return TQ_ERR_NULL;
+    const bool amax_given = (flags & TQ_AMAX_GIVEN) != 0;
+    hipStream_t s = as_stream(stream);
+    if (n == 0) {
+        clear_error();
+        tq::launch_empty_tensor_scalars(tensor_amax, tensor_scale, batch, !amax_given, s);
+        return launch_status();
+    }
+    if (!x || !codes || !scales)
+        return TQ_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(codes, 16))
+        return TQ_ERR_ALIGN;
+    clear_error();
+    if (!amax_given)
+        tq::launch_amax(x, dtype == TQ_BF16, batch, rows * cols, tensor_amax, s);
+    tq::launch_quantize_tile16(x, dtype == TQ_BF16, batch, rows, cols, tensor_amax, codes, scales,
+                               tensor_scale, s);
+    return launch_status();
+}
+
+TQ_API tq_status tq_transpose_tile16(const uint8_t* codes, const uint8_t* scales,
+                                     const float* tensor_scale, int64_t batch, int64_t rows,
+                                     int64_t cols, uint8_t* codes_t, uint8_t* scales_t,
+                                     float* tensor_scale_t, void* stream)
+{
+    int64_t n;
+    if (!product(batch, rows, cols, &n) || rows % 16 != 0 || cols % 16 != 0)
+        return TQ_ERR_SHAPE;
+    if (batch == 0)
+        return TQ_OK;
+    if (!tensor_scale || !tensor_scale_t)
+        return TQ_ERR_NULL;
+    if (n > 0) {
+        if (!codes || !scales || !codes_t || !scales_t)
+            return TQ_ERR_NULL;
+        if (!aligned(codes, 8) || !aligned(codes_t, 8))
+            return TQ_ERR_ALIGN;
+    }
+    clear_error();
+    tq::launch_transpose_tile16(codes, scales, tensor_scale, batch, rows, cols, codes_t, scales_t,
+                                tensor_scale_t, as_stream(stream));
+    return launch_status();
+}
+
 TQ_API tq_status tq_grouped_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales,
                                       const float* a_tensor_scale, const int32_t* group_offsets,
                                       int32_t num_groups, int64_t m_total, int64_t n, int64_t k,

@@ -27,6 +27,12 @@ void launch_requant_transpose_sr(const uint8_t* codes, const uint8_t* scales,
                                  const float* tensor_scale, int64_t batch, int64_t rows,
                                  int64_t cols, uint64_t seed, uint8_t* codes_t, uint8_t* scales_t,
                                  float* tensor_scale_t, hipStream_t s);
+void launch_quantize_tile16(const void* x, bool bf16, int64_t batch, int64_t rows, int64_t cols,
+                            const float* tensor_amax, uint8_t* codes, uint8_t* scales,
+                            float* tensor_scale, hipStream_t s);
+void launch_transpose_tile16(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                             int64_t batch, int64_t rows, int64_t cols, uint8_t* codes_t,
+                             uint8_t* scales_t, float* tensor_scale_t, hipStream_t s);
 void launch_grouped_gemm_nvfp4(const uint16_t* a, const int32_t* group_offsets, int num_groups,
                                int64_t m_total, int64_t n, int64_t k, const uint8_t* w_codes,
                                const uint8_t* w_scales, const float* w_tensor_scale, uint16_t* out,

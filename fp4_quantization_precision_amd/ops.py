@@ -192,6 +192,52 @@ def requant_transpose_sr(q: NVFP4, batch: int, rows: int, cols: int, seed: int,
     return out
 
 
+def quantize_tile16(x: torch.Tensor, amax_given: bool = False,
+                    out: Optional[NVFP4] = None) -> NVFP4:
+    """Nearest NVFP4 with one scale per 16x16 tile of x [..., rows, cols]; scales
+    [..., rows/16, cols/16]."""
+    _need(x, "x", (torch.float32, torch.bfloat16))
+    if x.dim() < 2:
+        raise ValueError("x must be [..., rows, cols]")
+    rows, cols = int(x.shape[-2]), int(x.shape[-1])
+    batch_shape = tuple(x.shape[:-2])
+    batch = 1
+    for d in batch_shape:
+        batch *= int(d)
+    if out is None:
+        dev = x.device
+        out = NVFP4(torch.empty(batch_shape + (rows, cols // 2), dtype=torch.uint8, device=dev),
+                    torch.empty(batch_shape + (rows // 16, cols // 16), dtype=torch.uint8, device=dev),
+                    torch.empty(batch, dtype=torch.float32, device=dev),
+                    torch.empty(batch, dtype=torch.float32, device=dev))
+    dtype = TQ_BF16 if x.dtype == torch.bfloat16 else TQ_F32
+    check(lib().tq_quantize_tile16(_p(x), dtype, batch, rows, cols, _p(out.tensor_amax),
+                                   _p(out.codes), _p(out.scales), _p(out.tensor_scale),
+                                   TQ_AMAX_GIVEN if amax_given else 0, _stream()),
+          "tq_quantize_tile16")
+    return out
+
+
+def transpose_tile16(q: NVFP4, batch: int, rows: int, cols: int,
+                     out: Optional[NVFP4] = None) -> NVFP4:
+    """Exact transpose of `batch` 16x16-tile NVFP4 tensors of rows x cols."""
+    _need(q.codes, "codes", (torch.uint8,))
+    _need(q.scales, "scales", (torch.uint8,))
+    _need(q.tensor_scale, "tensor_scale", (torch.float32,))
+    n = batch * rows * cols
+    if q.codes.numel() != n // 2 or q.scales.numel() != n // 256 or q.tensor_scale.numel() != batch:
+        raise ValueError("input buffers do not match batch x rows x cols")
+    if out is None:
+        dev = q.codes.device
+        out = NVFP4(torch.empty((batch, cols, rows // 2), dtype=torch.uint8, device=dev),
+                    torch.empty((batch, cols // 16, rows // 16), dtype=torch.uint8, device=dev),
+                    torch.empty(batch, dtype=torch.float32, device=dev), q.tensor_amax)
+    check(lib().tq_transpose_tile16(_p(q.codes), _p(q.scales), _p(q.tensor_scale), batch, rows,
+                                    cols, _p(out.codes), _p(out.scales), _p(out.tensor_scale),
+                                    _stream()), "tq_transpose_tile16")
+    return out
+
+
 def grouped_gemm_nvfp4(a: torch.Tensor, group_offsets: torch.Tensor, w: NVFP4, n: int, k: int,
                        out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """out[i] = bf16(s_e * a[i] @ W_e^T) for rows i of group e; W_e stored [n][k]."""

@@ -210,6 +210,44 @@ TQ_API tq_status tq_grouped_gemm_nvfp4(const uint16_t* a, const int32_t* group_o
                                        uint16_t* out, void* stream);
 
 /*
+ * tq_quantize_tile16 - nearest NVFP4 quantization with one E4M3 scale per 16 x 16
+ * tile instead of per 16 consecutive values ([TML] forward/backward-mismatch
+ * paragraph: the tile alternative, which a transpose leaves intact, and its
+ * drawback that one large value can zero the rest of its 256-value tile).
+ *
+ * Steps as tq_quantize with the block maximum taken over the tile:
+ *   s_t = A_T/2688; per tile A = max|x| over its 256 values,
+ *   e = enc(fl(fl(A/6)/s_t)), r = fl(1/fl(dec(e) s_t)); per element the nearest
+ *   E2M1 code of fl(x r), zero as +0; a tile whose scale decodes to 0 is all 0.
+ *
+ *   x            [batch][rows][cols] fp32 or bf16, 16-byte aligned.
+ *   codes        [batch][rows][cols/2] (as tq_quantize), 16-byte aligned.
+ *   scales       [batch][rows/16][cols/16] E4M3 tile scales.
+ *   tensor_amax, tensor_scale, flags as tq_quantize.
+ * Requires rows % 16 == 0 and cols % 16 == 0 (else TQ_ERR_SHAPE).
+ */
+TQ_API tq_status tq_quantize_tile16(const void* x, int32_t dtype, int64_t batch, int64_t rows,
+                                    int64_t cols, float* tensor_amax, uint8_t* codes,
+                                    uint8_t* scales, float* tensor_scale, uint32_t flags,
+                                    void* stream);
+
+/*
+ * tq_transpose_tile16 - transpose of a 16x16-tile NVFP4 tensor.  Every value keeps
+ * its tile, so codes and tile scales are moved and nothing is requantized: the
+ * result equals tq_quantize_tile16 of the transposed input, bit for bit.
+ *
+ *   codes/scales/tensor_scale  input as written by tq_quantize_tile16.
+ *   codes_t   [batch][cols][rows/2], 8-byte aligned (codes too).
+ *   scales_t  [batch][cols/16][rows/16].
+ *   tensor_scale_t [batch] = tensor_scale.
+ * Requires rows % 16 == 0 and cols % 16 == 0.
+ */
+TQ_API tq_status tq_transpose_tile16(const uint8_t* codes, const uint8_t* scales,
+                                     const float* tensor_scale, int64_t batch, int64_t rows,
+                                     int64_t cols, uint8_t* codes_t, uint8_t* scales_t,
+                                     float* tensor_scale_t, void* stream);
+
+/*
  * tq_grouped_gemm_w4a4 - MoE expert GEMM with NVFP4 weights AND NVFP4 activations
  * ([TRACE] results-table paragraph: the compared FP4 rollouts quantize weights,
  * activations and KV cache; [TML] summary box: the MoE forward runs in NVFP4).

@@ -159,6 +159,23 @@ def test_w4a4_gemm_validation(L):
     assert call(m=0) == TQ_OK and call(n=0) == TQ_OK
 
 
+def test_tile16_validation(L):
+    q = L.tq_quantize_tile16
+    assert q(P, 7, 1, 16, 32, P, P, P, P, 0, NULL) == TQ_ERR_DTYPE
+    assert q(P, TQ_BF16, 1, 24, 32, P, P, P, P, 0, NULL) == TQ_ERR_SHAPE   # rows % 16
+    assert q(P, TQ_BF16, 1, 16, 40, P, P, P, P, 0, NULL) == TQ_ERR_SHAPE   # cols % 16
+    assert q(P, TQ_BF16, 1, 16, 32, P, P, P, P, 2, NULL) == TQ_ERR_FLAGS
+    assert q(NULL, TQ_BF16, 1, 16, 32, P, P, P, P, 0, NULL) == TQ_ERR_NULL
+    assert q(P_MIS, TQ_BF16, 1, 16, 32, P, P, P, P, 0, NULL) == TQ_ERR_ALIGN
+    assert q(P, TQ_BF16, 0, 16, 32, P, P, P, P, 0, NULL) == TQ_OK
+    t = L.tq_transpose_tile16
+    assert t(P, P, P, 1, 24, 32, P, P, P, NULL) == TQ_ERR_SHAPE
+    assert t(NULL, P, P, 1, 16, 32, P, P, P, NULL) == TQ_ERR_NULL
+    assert t(P, P, NULL, 1, 16, 32, P, P, P, NULL) == TQ_ERR_NULL
+    assert t(C.c_void_p(0x7F0000000004), P, P, 1, 16, 32, P, P, P, NULL) == TQ_ERR_ALIGN
+    assert t(NULL, NULL, NULL, 0, 16, 32, NULL, NULL, NULL, NULL) == TQ_OK
+
+
 def test_other_validation(L):
     assert L.tq_tensor_amax(P, 9, 1, 32, P, NULL) == TQ_ERR_DTYPE
     assert L.tq_tensor_amax(P, TQ_BF16, 1, 24, P, NULL) == TQ_ERR_SHAPE
