@@ -74,6 +74,12 @@ def lib():
         L.tqo_sr_index.restype = i32
         L.tqo_requant_transpose_sr.argtypes = [p, p, p, i64, i64, i64, C.c_uint64, p, p, p]
         L.tqo_grouped_gemm.argtypes = [p, p, C.c_int32, i64, i64, p, p, p, p, i64, p, p]
+        L.tqo_e8m0_value.argtypes = [C.c_uint8]
+        L.tqo_e8m0_value.restype = C.c_double
+        L.tqo_e4m3_sr.argtypes = [C.c_float, i32]
+        L.tqo_e4m3_sr.restype = i32
+        L.tqo_quantize_mxfp8.argtypes = [p, i32, i64, i64, i64, p, p]
+        L.tqo_requant_transpose_mxfp8_sr.argtypes = [p, p, p, i64, i64, i64, C.c_uint64, p, p, p]
         L.tqo_quantize_tile16.argtypes = [p, i32, i64, i64, i64, i32, p, p, p, p]
         L.tqo_transpose_tile16.argtypes = [p, p, p, i64, i64, i64, p, p, p]
         L.tqo_grouped_gemm_w4a4.argtypes = [p, p, p, p, C.c_int32, i64, i64, p, p, p, p, i64, p, p]
@@ -251,6 +257,39 @@ def grouped_gemm(a, group_offsets, n: int, k: int, w_codes, w_scales, w_tensor_s
     lib().tqo_grouped_gemm(_ptr(A), _ptr(off), off.size - 1, n, k, _ptr(wc), _ptr(ws), _ptr(wt),
                            _ptr(rows), rows.size, _ptr(ref), _ptr(asum))
     return ref, asum
+
+
+def e8m0_value(b: int) -> float:
+    return lib().tqo_e8m0_value(int(b))
+
+
+def e4m3_sr(a: float, k: int) -> int:
+    return lib().tqo_e4m3_sr(float(a), int(k))
+
+
+def quantize_mxfp8(x, batch: int, rows: int, cols: int):
+    """Nearest MXFP8: codes [batch*rows*cols] E4M3 bytes, scales [batch*rows*cols/32] E8M0."""
+    a, dt = _x_and_dtype(x)
+    n = batch * rows * cols
+    codes = np.zeros(n, np.uint8)
+    scales = np.zeros(n // 32, np.uint8)
+    lib().tqo_quantize_mxfp8(_ptr(a), dt, batch, rows, cols, _ptr(codes), _ptr(scales))
+    return {"codes": codes, "scales": scales}
+
+
+def requant_transpose_mxfp8_sr(codes, scales, tensor_scale, batch: int, rows: int, cols: int,
+                               seed: int):
+    """NVFP4 [rows][cols] -> transposed MXFP8 [cols][rows] with stochastic rounding."""
+    c, s = _np(codes, np.uint8), _np(scales, np.uint8)
+    ts = _np(tensor_scale, np.float32)
+    n = batch * rows * cols
+    ct = np.zeros(n, np.uint8)
+    st = np.zeros(n // 32, np.uint8)
+    tst = np.zeros(batch, np.float32)
+    lib().tqo_requant_transpose_mxfp8_sr(_ptr(c), _ptr(s), _ptr(ts), batch, rows, cols,
+                                         C.c_uint64(seed & (2 ** 64 - 1)), _ptr(ct), _ptr(st),
+                                         _ptr(tst))
+    return {"codes": ct, "scales": st, "tensor_scale": tst}
 
 
 def quantize_tile16(x, batch: int, rows: int, cols: int, amax=None):

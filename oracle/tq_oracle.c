@@ -557,6 +557,146 @@ void tqo_grouped_gemm_w4a4(const uint8_t *a_codes, const uint8_t *a_scales,
 }
 
 /* ------------------------------------------------------------------------ */
+/* MXFP8: E4M3 elements, one E8M0 scale per 32 values                        */
+/* ------------------------------------------------------------------------ */
+
+/* [TML] summary box and format-comparison paragraph: the backward runs in
+ * MXFP8 at 8.25 bits per value, i.e. an 8-bit scale per 32 8-bit values.
+ * Readings (the usual MX convention): elements E4M3FN, the scale a power of
+ * two stored as a biased exponent byte E (value 2^(E-127)), the shared
+ * exponent of a block with maximum magnitude A > 0 being floor(log2 A) - 8
+ * (8 = exponent of E4M3's largest normal, 448 = 1.75 * 2^8), clamped to
+ * [-127, 127]; A = 0 gives E = 0 and zero elements. */
+double tqo_e8m0_value(uint8_t e)
+{
+    return ldexp(1.0, (int)e - 127);
+}
+
+static int mx_shared_exp(float A)
+{
+    int ex;
+    frexp((double)A, &ex); /* A = f * 2^ex, f in [0.5, 1): floor(log2 A) = ex - 1 */
+    int se = (ex - 1) - 8;
+    if (se < -127)
+        se = -127;
+    if (se > 127)
+        se = 127;
+    return se;
+}
+
+/* E4M3 byte (sign | magnitude code) of y: nearest, ties to even, saturating at
+ * 448, zero as +0. */
+static uint8_t e4m3_signed_nearest(float y)
+{
+    uint8_t m = tqo_e4m3_encode(fabsf(y));
+    return (uint8_t)((y < 0.0f && m != 0) ? (0x80 | m) : m);
+}
+
+/* Nearest MXFP8 quantization of `batch` tensors [rows][cols] (cols % 32 == 0):
+ * codes [batch][rows][cols] E4M3 bytes, scales [batch][rows][cols/32] E8M0. */
+void tqo_quantize_mxfp8(const void *x, int dtype, int64_t batch, int64_t rows, int64_t cols,
+                        uint8_t *codes, uint8_t *scales)
+{
+    const int64_t nb = cols / 32;
+    for (int64_t b = 0; b < batch; ++b)
+        for (int64_t r = 0; r < rows; ++r)
+            for (int64_t k = 0; k < nb; ++k) {
+                const int64_t base = (b * rows + r) * cols + 32 * k;
+                float A = 0.0f;
+                for (int t = 0; t < 32; ++t) {
+                    float v = fabsf(load_x(x, dtype, base + t));
+                    if (v > A)
+                        A = v;
+                }
+                const int64_t si = (b * rows + r) * nb + k;
+                if (A == 0.0f) {
+                    scales[si] = 0;
+                    for (int t = 0; t < 32; ++t)
+                        codes[base + t] = 0;
+                    continue;
+                }
+                const int se = mx_shared_exp(A);
+                scales[si] = (uint8_t)(se + 127);
+                for (int t = 0; t < 32; ++t) {
+                    /* exact scaling by a power of two (ldexpf), then E4M3 nearest */
+                    float y = ldexpf(load_x(x, dtype, base + t), -se);
+                    codes[base + t] = e4m3_signed_nearest(y);
+                }
+            }
+}
+
+/* E4M3 stochastic rounding of a >= 0 with random byte k: between the two E4M3
+ * values bracketing a, up iff k < 256 (a - lo) / (hi - lo) (the rule of
+ * tqo_sr_index on the E4M3 grid); values on the grid are kept and a >= 448
+ * gives 448. */
+int tqo_e4m3_sr(float a, int k)
+{
+    if (a >= 448.0f)
+        return 0x7E;
+    /* lo = largest E4M3 value <= a: scan the 127 finite codes (a slow, obvious search) */
+    int lo = 0;
+    for (int c = 0; c <= 0x7E; ++c)
+        if (tqo_e4m3_value((uint8_t)c) <= (double)a)
+            lo = c;
+    double vlo = tqo_e4m3_value((uint8_t)lo);
+    if (vlo == (double)a)
+        return lo;
+    double vhi = tqo_e4m3_value((uint8_t)(lo + 1));
+    double p256 = 256.0 * (((double)a - vlo) / (vhi - vlo)); /* exact */
+    return ((double)k < p256) ? lo + 1 : lo;
+}
+
+/* Backward copy for MXFP8: an NVFP4 tensor [rows][cols] is dequantized exactly
+ * (u = +-G[m] dec(e), tensor scale kept aside), transposed, and requantized to
+ * MXFP8 along the new rows (blocks of 32 down the old rows) with stochastic
+ * rounding ([TML] summary box: MXFP8 backward with requantization and
+ * stochastic rounding; forward/backward-mismatch paragraph).  Per new block:
+ * se = shared exponent of max|u|, y = u * 2^-se (exact), code = sign | E4M3 SR
+ * of |y| with the element's random byte (the stream of tqo_sr_byte at output
+ * index i = (b * cols + j) * rows + r).  The tensor scale is copied.
+ * Requires rows % 32 == 0, cols % 16 == 0.  codes_t [batch][cols][rows],
+ * scales_t [batch][cols][rows/32]. */
+void tqo_requant_transpose_mxfp8_sr(const uint8_t *codes, const uint8_t *scales,
+                                    const float *tensor_scale, int64_t batch, int64_t rows,
+                                    int64_t cols, uint64_t seed, uint8_t *codes_t,
+                                    uint8_t *scales_t, float *tensor_scale_t)
+{
+    const int64_t per_tensor = rows * cols;
+    for (int64_t b = 0; b < batch; ++b) {
+        tensor_scale_t[b] = tensor_scale[b];
+        for (int64_t j = 0; j < cols; ++j)
+            for (int64_t t = 0; t < rows / 32; ++t) {
+                float u[32];
+                float A = 0.0f;
+                for (int q = 0; q < 32; ++q) {
+                    int64_t r = 32 * t + q;
+                    int code = tqo_get_code(codes, b * per_tensor + r * cols + j);
+                    float v = (float)E2M1_GRID[code & 7] *
+                              (float)tqo_e4m3_value(scales[(b * rows + r) * (cols / 16) + j / 16]);
+                    u[q] = (code & 8) ? -v : v;
+                    if (fabsf(u[q]) > A)
+                        A = fabsf(u[q]);
+                }
+                const int64_t si = (b * cols + j) * (rows / 32) + t;
+                const int64_t o = (b * cols + j) * rows + 32 * t;
+                if (A == 0.0f) {
+                    scales_t[si] = 0;
+                    for (int q = 0; q < 32; ++q)
+                        codes_t[o + q] = 0;
+                    continue;
+                }
+                const int se = mx_shared_exp(A);
+                scales_t[si] = (uint8_t)(se + 127);
+                for (int q = 0; q < 32; ++q) {
+                    float y = ldexpf(u[q], -se);
+                    int m = tqo_e4m3_sr(fabsf(y), tqo_sr_byte(seed, (uint64_t)(o + q)));
+                    codes_t[o + q] = (uint8_t)((y < 0.0f && m != 0) ? (0x80 | m) : m);
+                }
+            }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* 16x16-tile scaling                                                        */
 /* ------------------------------------------------------------------------ */
 

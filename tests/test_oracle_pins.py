@@ -706,6 +706,111 @@ def test_w4a4_gemm_reduces_to_w4a16(orc):
 
 
 # ----------------------------------------------------------------------------------
+# MXFP8 (E4M3 elements, E8M0 scale per 32)
+# ----------------------------------------------------------------------------------
+
+E4M3_GRID = np.array(sorted(set(e4m3_decode_torch(np.arange(0x7F)).astype(np.float64))))
+
+
+def test_mxfp8_storage_is_8p25_bits(orc):
+    g = load("format_facts.json")
+    R, Cc = 4, 64
+    x = np.random.default_rng(1).standard_normal((R, Cc)).astype(np.float32)
+    q = orc.quantize_mxfp8(x, 1, R, Cc)
+    assert 8.0 * (q["codes"].nbytes + q["scales"].nbytes) / (R * Cc) == g["bits_per_value_mxfp8"]
+
+
+def test_mxfp8_shared_exponent_closed_form(orc):
+    # block maxima 1, 0.75, 448, 500, 2^-20: shared exponents -8, -9, 0, 0, -28
+    x = np.zeros((5, 32), np.float32)
+    for r, m in enumerate([1.0, 0.75, 448.0, 500.0, 2.0 ** -20]):
+        x[r, 0] = m
+        x[r, 1] = -m / 3
+    q = orc.quantize_mxfp8(x, 1, 5, 32)
+    assert list(q["scales"]) == [127 - 8, 127 - 9, 127, 127, 127 - 28]
+    c = q["codes"].reshape(5, 32)
+    assert c[2, 0] == 0x7E and c[3, 0] == 0x7E  # 448 exact; 500 saturates to 448
+    assert orc.e8m0_value(q["scales"][0]) == 2.0 ** -8
+    z = orc.quantize_mxfp8(np.zeros((1, 32), np.float32), 1, 1, 32)
+    assert z["scales"][0] == 0 and (z["codes"] == 0).all()
+
+
+def test_mxfp8_elements_match_torch_e4m3_cast(orc):
+    """Below saturation every element is torch's RNE float8_e4m3fn cast of the value
+    divided by its block's power-of-two scale (signed byte, zero as +0)."""
+    rng = np.random.default_rng(5)
+    R, Cc = 64, 256
+    x = (rng.standard_normal((R, Cc)) * np.exp2(rng.uniform(-12, 12, (R, 1)))).astype(np.float32)
+    q = orc.quantize_mxfp8(x, 1, R, Cc)
+    scale = np.repeat(np.array([orc.e8m0_value(b) for b in q["scales"]]).reshape(R, Cc // 32), 32, 1)
+    y = (x / scale).astype(np.float32)
+    ok = np.abs(y) < 448.0
+    ref = torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    ref = np.where((ref & 0x7F) == 0, 0, ref)  # -0 -> +0
+    assert np.array_equal(q["codes"].reshape(R, Cc)[ok], ref[ok])
+    assert ok.mean() > 0.99
+
+
+def test_e4m3_sr_bracket_and_bias(orc):
+    """E4M3 stochastic rounding: on-grid values are kept, others go to the lower or
+    upper neighbour on torch's E4M3 grid, and over all 256 random bytes the mean is
+    lo + (hi - lo) * ceil(256 p) / 256 with p = (a - lo)/(hi - lo): exactly unbiased
+    when 256 p is an integer."""
+    rng = np.random.default_rng(9)
+    a_vals = np.concatenate([E4M3_GRID[:-1] + (E4M3_GRID[1:] - E4M3_GRID[:-1]) * rng.random(126),
+                             E4M3_GRID[:-1] + (E4M3_GRID[1:] - E4M3_GRID[:-1]) * 0.25,
+                             E4M3_GRID]).astype(np.float32)
+    for a in a_vals:
+        a64 = float(a)
+        i = np.searchsorted(E4M3_GRID, a64, side="right") - 1
+        lo = E4M3_GRID[i]
+        codes = [orc.e4m3_sr(a, k) for k in range(256)]
+        vals = np.array([orc.e4m3_value(c) for c in codes])
+        if lo == a64 or a64 >= 448.0:
+            assert (vals == min(a64, 448.0)).all()
+            continue
+        hi = E4M3_GRID[i + 1]
+        assert set(vals) <= {lo, hi}
+        p256 = Fraction(a64 - lo) / Fraction(hi - lo) * 256
+        n_up = -(-p256.numerator // p256.denominator)  # ceil
+        assert int((vals == hi).sum()) == n_up
+    assert orc.e4m3_sr(500.0, 0) == 0x7E
+
+
+def test_mxfp8_sr_transpose_is_exact_on_representable_values(orc):
+    """NVFP4 values whose block scales are powers of two have at most 2 significant
+    bits, so after the power-of-two MX scaling they are E4M3 values: the stochastic
+    requantize must return the exact transpose for every seed."""
+    rng = np.random.default_rng(13)
+    R, Cc = 64, 48
+    codes = rng.integers(0, 256, R * Cc // 2, dtype=np.uint8)
+    scales = rng.choice(np.uint8([0x30, 0x38, 0x40, 0x48, 0x28]), R * Cc // 16)  # 2^-1 .. 2^2, 2^-2
+    ts = np.float32([0.7])
+    u = orc.dequantize(codes, scales, np.ones(1, np.float32), 1, R, Cc).reshape(R, Cc)
+    for seed in [0, 1, 2 ** 33 + 5]:
+        o = orc.requant_transpose_mxfp8_sr(codes, scales, ts, 1, R, Cc, seed)
+        assert o["tensor_scale"][0] == ts[0]
+        sc = np.repeat(np.array([orc.e8m0_value(b) for b in o["scales"]]).reshape(Cc, R // 32), 32, 1)
+        v = e4m3_decode_torch(o["codes"]).astype(np.float64).reshape(Cc, R) * sc
+        assert np.array_equal(v, u.T.astype(np.float64))
+
+
+def test_mxfp8_sr_transpose_unbiased_over_seeds(orc):
+    rng = np.random.default_rng(17)
+    R, Cc = 64, 32
+    codes = rng.integers(0, 256, R * Cc // 2, dtype=np.uint8)
+    scales = rng.integers(0x20, 0x50, R * Cc // 16, dtype=np.uint8)
+    u = orc.dequantize(codes, scales, np.ones(1, np.float32), 1, R, Cc).reshape(R, Cc).T
+    acc = np.zeros((Cc, R))
+    for seed in range(64):
+        o = orc.requant_transpose_mxfp8_sr(codes, scales, np.float32([1.0]), 1, R, Cc, seed)
+        sc = np.repeat(np.array([orc.e8m0_value(b) for b in o["scales"]]).reshape(Cc, R // 32), 32, 1)
+        acc += e4m3_decode_torch(o["codes"]).astype(np.float64).reshape(Cc, R) * sc
+    rel = (acc / 64 - u).sum() / np.abs(u).sum()
+    assert abs(rel) < 2e-3, rel
+
+
+# ----------------------------------------------------------------------------------
 # 16x16-tile scaling
 # ----------------------------------------------------------------------------------
 
