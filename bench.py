@@ -325,7 +325,9 @@ def measure_extras(L, dev, stream, A, OFF, QG, QN, nl, first_hint):
     * FP4 KV cache with hints: one layer's K and V cache [32768 x 8 x 128] bf16,
       rollout nearest + hints and trainer guided, per token-head blocks of 16;
     * 16x16-tile scaling: quantize and exact transpose of the activations
-      workload [32768 x 4096] bf16, and the share of zero codes against block-16."""
+      workload [32768 x 4096] bf16, and the share of zero codes against block-16;
+    * MXFP8 for the backward: nearest quantize of the activations workload and the
+      NVFP4 -> MXFP8 stochastic-rounding transpose of each layer's trainer weights."""
     import ctypes as C
 
     import torch
@@ -403,6 +405,42 @@ def measure_extras(L, dev, stream, A, OFF, QG, QN, nl, first_hint):
         "kernel": "tq::quantize_kernel<true, 2>", "avg_us": round(us_gd, 2),
         "GB/s": round(n * 2.6875 / us_gd / 1e3, 1),
         "frac_hbm_peak": round(n * 2.6875 / us_gd / 1e3 / HBM_PEAK_GBS, 4)}
+    # ---- MXFP8 backward: nearest quantize of activations, NVFP4 -> MXFP8 SR transpose ----
+    T3, H3 = 32768, 4096
+    xm, _, _ = inputs.activations(T3, H3, device=dev)
+    n3 = T3 * H3
+    mxc = torch.empty((T3, H3), dtype=torch.uint8, device=dev)
+    mxs = torch.empty((T3, H3 // 32), dtype=torch.uint8, device=dev)
+
+    def mx_quant():
+        assert L.tq_quantize_mxfp8(P(xm), TQ_BF16, 1, T3, H3, P(mxc), P(mxs), sp) == 0
+
+    per = ROWS * COLS
+    mct = torch.empty((EXPERTS, COLS, ROWS), dtype=torch.uint8, device=dev)
+    mst = torch.empty((EXPERTS, COLS, ROWS // 32), dtype=torch.uint8, device=dev)
+    mts = torch.empty(EXPERTS, dtype=torch.float32, device=dev)
+
+    def mx_transpose():
+        for l in range(nl):
+            w = QG if l >= first_hint else QN
+            assert L.tq_requant_transpose_mxfp8_sr(P(w.codes[l]), P(w.scales[l]), P(w.tensor_scale[l]),
+                                                   EXPERTS, ROWS, COLS, C.c_uint64(l), P(mct), P(mst),
+                                                   P(mts), sp) == 0
+
+    us_mq = _time_phase(stream, mx_quant, 5)
+    us_mt = _time_phase(stream, mx_transpose, 2) / nl
+    b_mq = n3 * (2 + 1 + 1 / 32)
+    b_mt = EXPERTS * per * (0.5625 + 1 + 1 / 32)
+    out["mxfp8_quantize"] = {
+        "kernel": "tq::quantize_mxfp8_kernel<true>", "avg_us": round(us_mq, 2),
+        "GB/s": round(b_mq / us_mq / 1e3, 1), "frac_hbm_peak": round(b_mq / us_mq / 1e3 / HBM_PEAK_GBS, 4),
+        "workload": f"activations [{T3} x {H3}] bf16"}
+    out["mxfp8_sr_transpose"] = {
+        "kernel": "tq::requant_transpose_mxfp8_sr_kernel", "avg_us": round(us_mt, 2),
+        "GB/s": round(b_mt / us_mt / 1e3, 1), "frac_hbm_peak": round(b_mt / us_mt / 1e3 / HBM_PEAK_GBS, 4),
+        "workload": f"one MoE layer of trainer NVFP4 weights {EXPERTS} x [{ROWS} x {COLS}] -> MXFP8 [{COLS} x {ROWS}]"}
+    del xm, mxc, mxs, mct, mst, mts
+
     # ---- 16x16-tile scaling on the activations workload ----
     T2, Hd = 32768, 4096
     xa, _, _ = inputs.activations(T2, Hd, device=dev)

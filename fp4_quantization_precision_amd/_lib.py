@@ -28,6 +28,8 @@ SIGNATURES = {
     "tq_quantize_guided": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _P, _U32, _P]),
     "tq_requant_transpose_sr": (_I32, [_P, _P, _P, _I64, _I64, _I64, C.c_uint64, _P, _P, _P, _P]),
     "tq_grouped_gemm_nvfp4": (_I32, [_P, _P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "tq_quantize_mxfp8": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _P]),
+    "tq_requant_transpose_mxfp8_sr": (_I32, [_P, _P, _P, _I64, _I64, _I64, C.c_uint64, _P, _P, _P, _P]),
     "tq_quantize_tile16": (_I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _U32, _P]),
     "tq_transpose_tile16": (_I32, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "tq_grouped_gemm_w4a4": (_I32, [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _P, _P, _P, _P, _P]),

@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["tq_api.cpp", "tq_quantize.hip", "tq_sr.hip", "tq_gemm.hip", "tq_tile16.hip"]
+SOURCES = ["tq_api.cpp", "tq_quantize.hip", "tq_sr.hip", "tq_gemm.hip", "tq_tile16.hip", "tq_mxfp8.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -186,6 +186,50 @@ TQ_API tq_status tq_grouped_gemm_nvfp4(const uint16_t* a, const int32_t* group_o
     return launch_status();
 }
 
+TQ_API tq_status tq_quantize_mxfp8(const void* x, int32_t dtype, int64_t batch, int64_t rows,
+                                   int64_t cols, uint8_t* codes, uint8_t* scales, void* stream)
+{
+    if (dtype != TQ_F32 && dtype != TQ_BF16)
+        return TQ_ERR_DTYPE;
+    int64_t n;
+    if (!product(batch, rows, cols, &n) || cols % 32 != 0)
+        return TQ_ERR_SHAPE;
+    if (n == 0)
+        return TQ_OK;
+    if (!x || !codes || !scales)
+        return TQ_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(codes, 16))
+        return TQ_ERR_ALIGN;
+    clear_error();
+    tq::launch_quantize_mxfp8(x, dtype == TQ_BF16, n, codes, scales, as_stream(stream));
+    return launch_status();
+}
+
+TQ_API tq_status tq_requant_transpose_mxfp8_sr(const uint8_t* codes, const uint8_t* scales,
+                                               const float* tensor_scale, int64_t batch,
+                                               int64_t rows, int64_t cols, uint64_t seed,
+                                               uint8_t* codes_t, uint8_t* scales_t,
+                                               float* tensor_scale_t, void* stream)
+{
+    int64_t n;
+    if (!product(batch, rows, cols, &n) || rows % 32 != 0 || cols % 16 != 0)
+        return TQ_ERR_SHAPE;
+    if (batch == 0)
+        return TQ_OK;
+    if (!tensor_scale || !tensor_scale_t)
+        return TQ_ERR_NULL;
+    if (n > 0) {
+        if (!codes || !scales || !codes_t || !scales_t)
+            return TQ_ERR_NULL;
+        if (!aligned(codes, 16) || !aligned(codes_t, 16))
+            return TQ_ERR_ALIGN;
+    }
+    clear_error();
+    tq::launch_requant_transpose_mxfp8_sr(codes, scales, tensor_scale, batch, rows, cols, seed,
+                                          codes_t, scales_t, tensor_scale_t, as_stream(stream));
+    return launch_status();
+}
+
 TQ_API tq_status tq_quantize_tile16(const void* x, int32_t dtype, int64_t batch, int64_t rows,
                                     int64_t cols, float* tensor_amax, uint8_t* codes,
                                     uint8_t* scales, float* tensor_scale, uint32_t flags,

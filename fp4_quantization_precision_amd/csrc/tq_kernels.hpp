@@ -33,6 +33,12 @@ void launch_quantize_tile16(const void* x, bool bf16, int64_t batch, int64_t row
 void launch_transpose_tile16(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
                              int64_t batch, int64_t rows, int64_t cols, uint8_t* codes_t,
                              uint8_t* scales_t, float* tensor_scale_t, hipStream_t s);
+void launch_quantize_mxfp8(const void* x, bool bf16, int64_t n, uint8_t* codes, uint8_t* scales,
+                           hipStream_t s);
+void launch_requant_transpose_mxfp8_sr(const uint8_t* codes, const uint8_t* scales,
+                                       const float* tensor_scale, int64_t batch, int64_t rows,
+                                       int64_t cols, uint64_t seed, uint8_t* codes_t,
+                                       uint8_t* scales_t, float* tensor_scale_t, hipStream_t s);
 void launch_grouped_gemm_nvfp4(const uint16_t* a, const int32_t* group_offsets, int num_groups,
                                int64_t m_total, int64_t n, int64_t k, const uint8_t* w_codes,
                                const uint8_t* w_scales, const float* w_tensor_scale, uint16_t* out,

@@ -1,0 +1,290 @@
+// tq_mxfp8.hip - MXFP8 (E4M3 elements, one E8M0 scale per 32 values) for the
+// backward: nearest quantization, and the NVFP4 -> MXFP8 transpose-requantize
+// with stochastic rounding (gfx950).
+//
+// [TML] "싱킹 머신스 랩, 4비트 학습 기법 공개", summary box (MXFP8 backward with
+// requantization and stochastic rounding), format-comparison paragraph (8.25
+// bits per value: an 8-bit scale per 32 8-bit values) and forward/backward-
+// mismatch paragraph.  Formats and readings in include/tq.h: the shared
+// exponent of a block with maximum A > 0 is floor(log2 A) - 8, clamped to
+// [-127, 127]; elements saturate at 448; zero is +0.
+//
+// Quantize: one lane per 32-value block (64 bytes of bf16 in, 32 code bytes and
+// one scale byte out).  Transpose: tiles of 128 input rows x 256 input columns
+// staged through LDS exactly as in the NVFP4 transpose; each thread then owns
+// one output row and two new blocks of 32 (its 64 values of the tile), with
+// two Philox4x32-10 calls per block for the 32 random bytes.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq_device.hpp"
+#include "tq_kernels.hpp"
+
+namespace tq {
+
+// Shared exponent of a block with maximum magnitude A > 0: floor(log2 A) - 8,
+// clamped to [-127, 127] (frexp handles subnormal A).
+__device__ __forceinline__ int mx_shared_exp(float A)
+{
+    const int e = __builtin_amdgcn_frexp_expf(A) - 1 - 8;
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// E4M3 byte of y: nearest, ties to even, saturating at 448, zero as +0.
+__device__ __forceinline__ uint32_t e4m3_signed_nearest(float y)
+{
+    const uint32_t m = e4m3_encode(fabsf(y));
+    return (y < 0.0f && m != 0u) ? (0x80u | m) : m;
+}
+
+// E4M3 stochastic rounding of a >= 0 with random byte k: floor grid point from
+// the bits (3 mantissa bits from 2^-6 up, multiples of 2^-9 below), step up iff
+// G_lo + k * step / 256 < a (all terms exact); a >= 448 gives 448.
+__device__ __forceinline__ uint32_t e4m3_sr_code(float a, float k)
+{
+    if (a >= 448.0f)
+        return 0x7Eu;
+    uint32_t lo;
+    float glo, q;  // q = spacing / 256
+    if (a >= 0x1p-6f) {
+        const uint32_t bits = __float_as_uint(a) & 0xFFF00000u;
+        glo = __uint_as_float(bits);
+        q = __uint_as_float((bits & 0x7F800000u) - ((3u + 8u) << 23));
+        lo = ((((bits >> 23) & 0xFFu) - 120u) << 3) | ((bits >> 20) & 7u);
+    } else {
+        const float f = __builtin_floorf(a * 512.0f);  // exact: a * 2^9 and its floor
+        glo = f * 0x1p-9f;
+        q = 0x1p-17f;
+        lo = (uint32_t)f;
+    }
+    return lo + ((glo + k * q < a) ? 1u : 0u);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const void* __restrict__ x,
+                                                             int64_t blocks, uint4* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales)
+{
+    for (int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x; blk < blocks;
+         blk += (int64_t)gridDim.x * 256) {
+        float v[32];
+        if (BF16) {
+            const uint4* p = static_cast<const uint4*>(x) + 4 * blk;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const uint4 q = p[h];
+                const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    v[8 * h + 2 * i] = bf16_lo(w[i]);
+                    v[8 * h + 2 * i + 1] = bf16_hi(w[i]);
+                }
+            }
+        } else {
+            const float4* p = static_cast<const float4*>(x) + 8 * blk;
+#pragma unroll
+            for (int h = 0; h < 8; ++h) {
+                const float4 q = p[h];
+                v[4 * h] = q.x;
+                v[4 * h + 1] = q.y;
+                v[4 * h + 2] = q.z;
+                v[4 * h + 3] = q.w;
+            }
+        }
+        float A = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            A = fmaxf(A, fabsf(v[i]));
+        uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        uint32_t sb = 0;
+        if (A != 0.0f) {
+            const int se = mx_shared_exp(A);
+            sb = (uint32_t)(se + 127);
+#pragma unroll
+            for (int i = 0; i < 32; ++i)
+                w[i >> 2] |= e4m3_signed_nearest(__builtin_ldexpf(v[i], -se)) << (8 * (i & 3));
+        }
+        codes[2 * blk] = make_uint4(w[0], w[1], w[2], w[3]);
+        codes[2 * blk + 1] = make_uint4(w[4], w[5], w[6], w[7]);
+        scales[blk] = (uint8_t)sb;
+    }
+}
+
+constexpr int kMTR = 128, kMTC = 256, kMThreads = 512, kMLdsStride = 68;
+
+__device__ __forceinline__ int mlds_slot(int c, int p) { return c * kMLdsStride + (p ^ (8 * (c >> 5))); }
+
+__global__ __launch_bounds__(kMThreads, 2) void requant_transpose_mxfp8_sr_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+    const float* __restrict__ tensor_scale, int64_t batch, int64_t rows, int64_t cols,
+    uint32_t seed_lo, uint32_t seed_hi, uint8_t* __restrict__ codes_t,
+    uint8_t* __restrict__ scales_t, float* __restrict__ tensor_scale_t, int64_t tiles_r,
+    int64_t tiles_c, int vec_in)
+{
+    __shared__ __attribute__((aligned(16))) uint32_t u_s[kMTC * kMLdsStride];
+    const int64_t tiles_per_tensor = tiles_r * tiles_c;
+    const int64_t total_tiles = tiles_per_tensor * batch;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int64_t sc_pitch = cols / 16, sct_pitch = rows / 32;
+
+    for (int64_t tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
+        const int64_t b = tile / tiles_per_tensor;
+        const int64_t rem = tile - b * tiles_per_tensor;
+        const int64_t tc = rem / tiles_r, tr = rem - tc * tiles_r;
+        const int64_t r0 = tr * kMTR, c0 = tc * kMTC;
+        const int rows_valid = (int)(rows - r0 < kMTR ? rows - r0 : kMTR);  // multiples of 32
+        const int cols_valid = (int)(cols - c0 < kMTC ? cols - c0 : kMTC);  // multiples of 16
+        if (tr == 0 && tc == 0 && tid == 0)
+            tensor_scale_t[b] = tensor_scale[b];
+
+        // ---- load + exact dequant: input rows (2p, 2p+1), columns [32h, 32h + 32) ----
+        {
+            const int p = 8 * wave + (lane >> 3), h = lane & 7, cl = 32 * h;
+            int nb = (cols_valid - cl) / 16;
+            nb = nb < 0 ? 0 : (nb > 2 ? 2 : nb);
+            uint32_t w[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+            float d[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
+            if (2 * p < rows_valid && nb > 0) {
+#pragma unroll
+                for (int rr = 0; rr < 2; ++rr) {
+                    const int64_t grow = b * rows + r0 + 2 * p + rr;
+                    const uint8_t* src = codes + (grow * cols + c0 + cl) / 2;
+                    if (vec_in && nb == 2) {
+                        const uint4 q = *reinterpret_cast<const uint4*>(src);
+                        w[rr][0] = q.x; w[rr][1] = q.y; w[rr][2] = q.z; w[rr][3] = q.w;
+                    } else {
+                        const uint2 q0 = *reinterpret_cast<const uint2*>(src);
+                        w[rr][0] = q0.x; w[rr][1] = q0.y;
+                        if (nb == 2) {
+                            const uint2 q1 = reinterpret_cast<const uint2*>(src)[1];
+                            w[rr][2] = q1.x; w[rr][3] = q1.y;
+                        }
+                    }
+                    const uint8_t* sp = scales + grow * sc_pitch + (c0 + cl) / 16;
+                    d[rr][0] = e4m3_decode(sp[0]);
+                    if (nb == 2)
+                        d[rr][1] = e4m3_decode(sp[1]);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float da = d[0][j >> 1], db = d[1][j >> 1];
+                const tq_f32x2 a0 = fp4x2_to_f32<0>(w[0][j]), a1 = fp4x2_to_f32<1>(w[0][j]);
+                const tq_f32x2 a2 = fp4x2_to_f32<2>(w[0][j]), a3 = fp4x2_to_f32<3>(w[0][j]);
+                const tq_f32x2 b0 = fp4x2_to_f32<0>(w[1][j]), b1 = fp4x2_to_f32<1>(w[1][j]);
+                const tq_f32x2 b2 = fp4x2_to_f32<2>(w[1][j]), b3 = fp4x2_to_f32<3>(w[1][j]);
+                const float va[8] = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
+                const float vb[8] = {b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    u_s[mlds_slot(cl + 8 * j + e, p)] = pack_hi16(va[e] * da, vb[e] * db);
+            }
+        }
+        __syncthreads();
+
+        // ---- requantize: thread -> output row c0 + c, input rows [64 half, 64 half + 64) ----
+        {
+            const int c = tid & (kMTC - 1), half = tid >> 8, h = c >> 5;
+            const int64_t oc = c0 + c;
+            if (c < cols_valid) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int lr = 64 * half + 32 * q;  // first local input row of the block
+                    if (lr >= rows_valid)
+                        continue;
+                    float u[32];
+#pragma unroll
+                    for (int part = 0; part < 2; ++part) {
+                        const uint4* src = reinterpret_cast<const uint4*>(
+                            u_s + c * kMLdsStride + 8 * ((4 * half + 2 * q + part) ^ h));
+                        const uint4 v0 = src[0], v1 = src[1];
+                        const uint32_t pk[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) {
+                            u[16 * part + 2 * i] = bf16_lo(pk[i]);
+                            u[16 * part + 2 * i + 1] = bf16_hi(pk[i]);
+                        }
+                    }
+                    float A = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 32; ++i)
+                        A = fmaxf(A, fabsf(u[i]));
+                    const int64_t obase = (b * cols + oc) * rows + r0 + lr;  // output linear index
+                    uint32_t wout[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                    uint32_t sb = 0;
+                    if (A != 0.0f) {
+                        const int se = mx_shared_exp(A);
+                        sb = (uint32_t)(se + 127);
+#pragma unroll
+                        for (int part = 0; part < 2; ++part) {
+                            const uint64_t beta = (uint64_t)(obase / 16) + part;
+                            const u32x4 rnd = philox4x32_10((uint32_t)beta, (uint32_t)(beta >> 32), 0u,
+                                                            0u, seed_lo, seed_hi);
+                            const uint32_t rw[4] = {rnd.x, rnd.y, rnd.z, rnd.w};
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) {
+                                const float y = __builtin_ldexpf(u[16 * part + i], -se);
+                                const float k = (float)((rw[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+                                const uint32_t m = e4m3_sr_code(fabsf(y), k);
+                                const uint32_t code = (y < 0.0f && m != 0u) ? (0x80u | m) : m;
+                                const int e = 16 * part + i;
+                                wout[e >> 2] |= code << (8 * (e & 3));
+                            }
+                        }
+                    }
+                    uint4* orow = reinterpret_cast<uint4*>(codes_t + obase);
+                    orow[0] = make_uint4(wout[0], wout[1], wout[2], wout[3]);
+                    orow[1] = make_uint4(wout[4], wout[5], wout[6], wout[7]);
+                    scales_t[(b * cols + oc) * sct_pitch + (r0 + lr) / 32] = (uint8_t)sb;
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+__global__ void mx_copy_scalars_kernel(const float* __restrict__ src, float* __restrict__ dst, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        dst[i] = src[i];
+}
+
+void launch_quantize_mxfp8(const void* x, bool bf16, int64_t n, uint8_t* codes, uint8_t* scales,
+                           hipStream_t s)
+{
+    const int64_t blocks = n / 32;
+    if (blocks == 0)
+        return;
+    int64_t g = (blocks + 255) / 256;
+    g = g < 4096 ? g : 4096;
+    uint4* c4 = reinterpret_cast<uint4*>(codes);
+    if (bf16)
+        hipLaunchKernelGGL(quantize_mxfp8_kernel<true>, dim3((unsigned)g), dim3(256), 0, s, x, blocks,
+                           c4, scales);
+    else
+        hipLaunchKernelGGL(quantize_mxfp8_kernel<false>, dim3((unsigned)g), dim3(256), 0, s, x, blocks,
+                           c4, scales);
+}
+
+void launch_requant_transpose_mxfp8_sr(const uint8_t* codes, const uint8_t* scales,
+                                       const float* tensor_scale, int64_t batch, int64_t rows,
+                                       int64_t cols, uint64_t seed, uint8_t* codes_t,
+                                       uint8_t* scales_t, float* tensor_scale_t, hipStream_t s)
+{
+    const int64_t tiles_r = (rows + kMTR - 1) / kMTR, tiles_c = (cols + kMTC - 1) / kMTC;
+    const int64_t total = tiles_r * tiles_c * batch;
+    if (total == 0) {
+        if (batch > 0)
+            hipLaunchKernelGGL(mx_copy_scalars_kernel, dim3(1), dim3(256), 0, s, tensor_scale,
+                               tensor_scale_t, batch);
+        return;
+    }
+    const int64_t g = total < (1 << 20) ? total : (1 << 20);
+    hipLaunchKernelGGL(requant_transpose_mxfp8_sr_kernel, dim3((unsigned)g), dim3(kMThreads), 0, s,
+                       codes, scales, tensor_scale, batch, rows, cols, (uint32_t)seed,
+                       (uint32_t)(seed >> 32), codes_t, scales_t, tensor_scale_t, tiles_r, tiles_c,
+                       (int)(cols % 32 == 0));
+}
+
+}  // namespace tq

@@ -192,6 +192,46 @@ def requant_transpose_sr(q: NVFP4, batch: int, rows: int, cols: int, seed: int,
     return out
 
 
+class MXFP8(NamedTuple):
+    codes: torch.Tensor         # [..., rows, cols] E4M3 bytes
+    scales: torch.Tensor        # [..., rows, cols/32] E8M0 bytes
+    tensor_scale: Optional[torch.Tensor] = None  # carried by the transposed backward copy
+
+
+def quantize_mxfp8(x: torch.Tensor) -> MXFP8:
+    """Nearest MXFP8 of x [..., rows, cols] (cols % 32 == 0)."""
+    _need(x, "x", (torch.float32, torch.bfloat16))
+    cols = int(x.shape[-1])
+    n = x.numel()
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(tuple(x.shape[:-1]) + (cols // 32,), dtype=torch.uint8, device=x.device)
+    dtype = TQ_BF16 if x.dtype == torch.bfloat16 else TQ_F32
+    rows = n // cols if cols else 0
+    check(lib().tq_quantize_mxfp8(_p(x), dtype, 1, rows, cols, _p(codes), _p(scales), _stream()),
+          "tq_quantize_mxfp8")
+    return MXFP8(codes, scales)
+
+
+def requant_transpose_mxfp8_sr(q: NVFP4, batch: int, rows: int, cols: int, seed: int) -> MXFP8:
+    """NVFP4 [batch][rows][cols] -> transposed MXFP8 [batch][cols][rows] with
+    stochastic rounding; the tensor scale is carried in the result."""
+    _need(q.codes, "codes", (torch.uint8,))
+    _need(q.scales, "scales", (torch.uint8,))
+    _need(q.tensor_scale, "tensor_scale", (torch.float32,))
+    n = batch * rows * cols
+    if q.codes.numel() != n // 2 or q.scales.numel() != n // 16 or q.tensor_scale.numel() != batch:
+        raise ValueError("input buffers do not match batch x rows x cols")
+    dev = q.codes.device
+    out = MXFP8(torch.empty((batch, cols, rows), dtype=torch.uint8, device=dev),
+                torch.empty((batch, cols, rows // 32), dtype=torch.uint8, device=dev),
+                torch.empty(batch, dtype=torch.float32, device=dev))
+    check(lib().tq_requant_transpose_mxfp8_sr(_p(q.codes), _p(q.scales), _p(q.tensor_scale), batch,
+                                              rows, cols, C.c_uint64(seed & (2 ** 64 - 1)),
+                                              _p(out.codes), _p(out.scales), _p(out.tensor_scale),
+                                              _stream()), "tq_requant_transpose_mxfp8_sr")
+    return out
+
+
 def quantize_tile16(x: torch.Tensor, amax_given: bool = False,
                     out: Optional[NVFP4] = None) -> NVFP4:
     """Nearest NVFP4 with one scale per 16x16 tile of x [..., rows, cols]; scales

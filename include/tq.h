@@ -210,6 +210,47 @@ TQ_API tq_status tq_grouped_gemm_nvfp4(const uint16_t* a, const int32_t* group_o
                                        uint16_t* out, void* stream);
 
 /*
+ * MXFP8 ([TML] summary box: the backward runs in MXFP8 with requantization and
+ * stochastic rounding; format-comparison paragraph: 8.25 bits per value, i.e.
+ * an 8-bit scale per 32 8-bit values).  Elements are E4M3FN bytes (sign in bit 7,
+ * zero always 0x00, never NaN, |value| <= 448); a block of 32 consecutive values
+ * along a row shares one E8M0 scale byte E, value 2^(E - 127).  The shared
+ * exponent of a block with maximum magnitude A > 0 is floor(log2 A) - 8 (the
+ * exponent of E4M3's largest normal), clamped to [-127, 127]; A = 0 gives E = 0
+ * and zero elements.
+ *
+ * tq_quantize_mxfp8 - nearest MXFP8: element = E4M3 round-to-nearest-even of
+ * x * 2^-se, saturating at 448.
+ *   x       [batch][rows][cols] fp32 or bf16, 16-byte aligned.
+ *   codes   [batch][rows][cols] E4M3 bytes, 16-byte aligned.
+ *   scales  [batch][rows][cols/32] E8M0 bytes.
+ * Requires cols % 32 == 0.
+ */
+TQ_API tq_status tq_quantize_mxfp8(const void* x, int32_t dtype, int64_t batch, int64_t rows,
+                                   int64_t cols, uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * tq_requant_transpose_mxfp8_sr - the backward copy of an NVFP4 forward tensor:
+ * dequantize exactly (u = +-G[m] * dec(e), tensor scale kept aside), transpose,
+ * and requantize to MXFP8 along the new rows (blocks of 32 down 32 original rows)
+ * with stochastic rounding on the E4M3 grid: y = u * 2^-se (exact); with lo <= |y|
+ * < hi the bracketing E4M3 values, round up iff k < 256 (|y| - lo) / (hi - lo),
+ * k the element's random byte from the Philox4x32-10 stream of
+ * tq_requant_transpose_sr (same counter, key and byte layout, output index
+ * i = (b * cols + j) * rows + r); |y| >= 448 gives 448.  The tensor scale is
+ * copied: value = E4M3 * 2^se * tensor_scale_t.
+ *   codes, scales, tensor_scale  NVFP4 input [batch][rows][cols] (as tq_quantize).
+ *   codes_t   [batch][cols][rows] E4M3 bytes; scales_t [batch][cols][rows/32] E8M0;
+ *   tensor_scale_t [batch].
+ * Requires rows % 32 == 0 and cols % 16 == 0; codes and codes_t 16-byte aligned.
+ */
+TQ_API tq_status tq_requant_transpose_mxfp8_sr(const uint8_t* codes, const uint8_t* scales,
+                                               const float* tensor_scale, int64_t batch,
+                                               int64_t rows, int64_t cols, uint64_t seed,
+                                               uint8_t* codes_t, uint8_t* scales_t,
+                                               float* tensor_scale_t, void* stream);
+
+/*
  * tq_quantize_tile16 - nearest NVFP4 quantization with one E4M3 scale per 16 x 16
  * tile instead of per 16 consecutive values ([TML] forward/backward-mismatch
  * paragraph: the tile alternative, which a transpose leaves intact, and its

@@ -633,11 +633,16 @@ int tqo_e4m3_sr(float a, int k)
 {
     if (a >= 448.0f)
         return 0x7E;
-    /* lo = largest E4M3 value <= a: scan the 127 finite codes (a slow, obvious search) */
-    int lo = 0;
-    for (int c = 0; c <= 0x7E; ++c)
-        if (tqo_e4m3_value((uint8_t)c) <= (double)a)
-            lo = c;
+    /* lo = largest code with value <= a: the finite codes 0x00..0x7E increase in
+     * value with the code, so bisect over them */
+    int lo = 0, hi_c = 0x7E;
+    while (lo < hi_c) {
+        int mid = (lo + hi_c + 1) / 2;
+        if (tqo_e4m3_value((uint8_t)mid) <= (double)a)
+            lo = mid;
+        else
+            hi_c = mid - 1;
+    }
     double vlo = tqo_e4m3_value((uint8_t)lo);
     if (vlo == (double)a)
         return lo;

@@ -159,6 +159,23 @@ def test_w4a4_gemm_validation(L):
     assert call(m=0) == TQ_OK and call(n=0) == TQ_OK
 
 
+def test_mxfp8_validation(L):
+    q = L.tq_quantize_mxfp8
+    assert q(P, 5, 1, 4, 64, P, P, NULL) == TQ_ERR_DTYPE
+    assert q(P, TQ_BF16, 1, 4, 48, P, P, NULL) == TQ_ERR_SHAPE  # cols % 32
+    assert q(NULL, TQ_BF16, 1, 4, 64, P, P, NULL) == TQ_ERR_NULL
+    assert q(P, TQ_BF16, 1, 4, 64, P, NULL, NULL) == TQ_ERR_NULL
+    assert q(P_MIS, TQ_BF16, 1, 4, 64, P, P, NULL) == TQ_ERR_ALIGN
+    assert q(NULL, TQ_BF16, 0, 4, 64, NULL, NULL, NULL) == TQ_OK
+    t = L.tq_requant_transpose_mxfp8_sr
+    assert t(P, P, P, 1, 48, 32, 0, P, P, P, NULL) == TQ_ERR_SHAPE   # rows % 32
+    assert t(P, P, P, 1, 64, 24, 0, P, P, P, NULL) == TQ_ERR_SHAPE   # cols % 16
+    assert t(P, P, NULL, 1, 64, 32, 0, P, P, P, NULL) == TQ_ERR_NULL
+    assert t(NULL, P, P, 1, 64, 32, 0, P, P, P, NULL) == TQ_ERR_NULL
+    assert t(P_MIS, P, P, 1, 64, 32, 0, P, P, P, NULL) == TQ_ERR_ALIGN
+    assert t(NULL, NULL, NULL, 0, 64, 32, 0, NULL, NULL, NULL, NULL) == TQ_OK
+
+
 def test_tile16_validation(L):
     q = L.tq_quantize_tile16
     assert q(P, 7, 1, 16, 32, P, P, P, P, 0, NULL) == TQ_ERR_DTYPE

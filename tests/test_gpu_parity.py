@@ -363,6 +363,73 @@ def test_kv_cache_full_size(which):
 
 
 # ----------------------------------------------------------------------------------
+# MXFP8 for the backward
+# ----------------------------------------------------------------------------------
+
+MX_SHAPES = [(1, 1, 32, "f32"), (1, 4, 64, "bf16"), (3, 17, 96, "bf16"), (2, 5, 1056, "f32"),
+             (1, 257, 512, "bf16")]
+
+
+@pytest.mark.parametrize("shape", MX_SHAPES)
+def test_mxfp8_quantize_shapes(shape):
+    B, R, Cc, dt = shape
+    rng = np.random.default_rng(R * 31 + Cc)
+    x = (rng.standard_normal((B, R, Cc)) * np.exp2(rng.uniform(-30, 30, (B, R, 1)))).astype(np.float32)
+    x[rng.random(x.shape) < 0.01] *= 1000
+    x.reshape(-1)[:32] = 0.0                     # an all-zero block
+    x.reshape(-1)[32:64] *= 2.0 ** -120           # a block near the bottom of the range
+    xt = torch.from_numpy(x)
+    if dt == "bf16":
+        xt = xt.to(torch.bfloat16)
+    q = ops.quantize_mxfp8(xt.to(DEV))
+    torch.cuda.synchronize()
+    o = oracle.quantize_mxfp8(xt, B, R, Cc)
+    assert np.array_equal(npu8(q.codes), o["codes"])
+    assert np.array_equal(npu8(q.scales), o["scales"])
+
+
+def test_mxfp8_quantize_activations_full_size():
+    T, Hd = 32768, 4096
+    xr, _, _ = inputs.activations(T, Hd, device=DEV)
+    q = ops.quantize_mxfp8(xr)
+    torch.cuda.synchronize()
+    o = oracle.quantize_mxfp8(xr.cpu(), 1, T, Hd)
+    assert np.array_equal(npu8(q.codes), o["codes"])
+    assert np.array_equal(npu8(q.scales), o["scales"])
+
+
+MX_SR_SHAPES = [(1, 32, 16), (1, 64, 80), (3, 288, 96), (2, 32, 1040), (1, 1024, 1024)]
+
+
+@pytest.mark.parametrize("shape", MX_SR_SHAPES)
+def test_mxfp8_sr_transpose_shapes(shape):
+    B, R, Cc = shape
+    c, s, ts = inputs.random_nvfp4(B, R, Cc, seed=R + 3 * Cc, zero_block_frac=0.05)
+    q = ops.NVFP4(c.to(DEV), s.to(DEV), ts.to(DEV), torch.zeros(B, device=DEV))
+    for seed in [0, 2 ** 40 + 3]:
+        t = ops.requant_transpose_mxfp8_sr(q, B, R, Cc, seed)
+        torch.cuda.synchronize()
+        o = oracle.requant_transpose_mxfp8_sr(c, s, ts, B, R, Cc, seed)
+        assert np.array_equal(npu8(t.codes), o["codes"]), f"{shape} seed {seed}"
+        assert np.array_equal(npu8(t.scales), o["scales"]), f"{shape} seed {seed}"
+        assert np.array_equal(npu8(t.tensor_scale), o["tensor_scale"])
+
+
+def test_mxfp8_sr_transpose_full_size():
+    """The 8192^2 transpose source, nearest NVFP4, then the MXFP8 backward copy."""
+    N = 8192
+    x = inputs.transpose_source(N, N, device=DEV)
+    q = ops.quantize(x)
+    t = ops.requant_transpose_mxfp8_sr(q, 1, N, N, seed=11)
+    torch.cuda.synchronize()
+    o = oracle.quantize(x.cpu(), 1, N, N)
+    assert_q_equal(q, o, "8192^2 nearest")
+    ot = oracle.requant_transpose_mxfp8_sr(o["codes"], o["scales"], o["tensor_scale"], 1, N, N, 11)
+    assert np.array_equal(npu8(t.codes), ot["codes"])
+    assert np.array_equal(npu8(t.scales), ot["scales"])
+
+
+# ----------------------------------------------------------------------------------
 # 16x16-tile scaling
 # ----------------------------------------------------------------------------------
 
