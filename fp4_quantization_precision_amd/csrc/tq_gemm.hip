@@ -69,14 +69,9 @@ __device__ __forceinline__ int swz(int r, int j)
 }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
-}
 
 // Eight codes (one dword, element 2j in the low nibble of byte j) times the
 // block scale d as four dwords of bf16 pairs.  Exact.
@@ -344,6 +339,7 @@ __global__ __launch_bounds__(kGThreads, kOcc) void grouped_gemm_nvfp4_kernel(
     };
 
     const int wm = wave >> 1, wn = wave & 1;
+    const bool live[2] = {row0 + 64 * wm < row_end, row0 + 64 * wm + 32 < row_end};
     f32x16_t acc[2][kNJ];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -401,9 +397,10 @@ __global__ __launch_bounds__(kGThreads, kOcc) void grouped_gemm_nvfp4_kernel(
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
+                if (live[i])  // 32-row blocks past the group's end only feed unstored rows
 #pragma unroll
-                for (int j = 0; j < kNJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                    for (int j = 0; j < kNJ; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
         }
         __syncthreads();
         if (more) {
@@ -420,16 +417,28 @@ __global__ __launch_bounds__(kGThreads, kOcc) void grouped_gemm_nvfp4_kernel(
 
     // ---- epilogue: scale, RNE to bf16, stage the tile in LDS, coalesced stores ----
     const float s_e = A_FP4 ? w_tensor_scale[e] * a_tensor_scale[0] : w_tensor_scale[e];
-    uint16_t* Cs = reinterpret_cast<uint16_t*>(smem);
+    // Lane l holds column l % 32 of rows R (register r, even) and R + 1 (r + 1).
+    // Neighbouring lanes swap one value (DPP quad_perm [1,0,3,2]) so that each
+    // writes one dword of two adjacent columns: the even lane row R at columns
+    // (c, c+1), the odd lane row R + 1 at columns (c-1, c).  The pair is rounded
+    // to bf16 (nearest even) by one packed conversion.
+    uint32_t* Cw = reinterpret_cast<uint32_t*>(smem);
+    const bool odd = lane & 1;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < kNJ; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const int col = (kBN / 2) * wn + 32 * j + (lane & 31);
-                Cs[row * kCLd + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][r] * s_e);
+            for (int r = 0; r < 16; r += 2) {
+                const float v0 = acc[i][j][r] * s_e, v1 = acc[i][j][r + 1] * s_e;
+                const float send = odd ? v0 : v1;
+                const float recv = __int_as_float(
+                    __builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
+                const f32x2_t pair = {odd ? recv : v0, odd ? v1 : recv};
+                const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(pair, bf16x2_t));
+                const int row = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) + (odd ? 1 : 0);
+                const int col = (kBN / 2) * wn + 32 * j + (lane & 31) - (odd ? 1 : 0);
+                Cw[(row * kCLd + col) >> 1] = w;
             }
     __syncthreads();
     const bool vec_ok = (n % 8) == 0;
@@ -440,7 +449,7 @@ __global__ __launch_bounds__(kGThreads, kOcc) void grouped_gemm_nvfp4_kernel(
         const int64_t gr = row0 + r, gc = col0 + 8 * c8;
         if (gr >= row_end || gc >= n)
             continue;
-        const uint4 v = *reinterpret_cast<const uint4*>(Cs + r * kCLd + 8 * c8);
+        const uint4 v = *reinterpret_cast<const uint4*>(Cw + ((r * kCLd + 8 * c8) >> 1));
         uint16_t* dst = out + gr * n + gc;
         if (vec_ok && gc + 8 <= n) {
             *reinterpret_cast<uint4*>(dst) = v;
