@@ -2,16 +2,22 @@
 //
 // [TML] "싱킹 머신스 랩, 4비트 학습 기법 공개", summary box and the paragraph on
 // where 4-bit compute is used: the MoE layers' forward runs with NVFP4 operands.
-// Here the weights are NVFP4 and the activations bf16: each weight tile is
-// dequantized exactly into LDS (G[m] * dec(e) has at most 6 significant bits, so
-// bf16 holds it), the products go through bf16 MFMA with fp32 accumulation, and
-// the per-expert fp32 tensor scale is applied once in the epilogue before the
-// round-to-nearest-even conversion to bf16.
+// Here the weights are NVFP4 and the activations bf16: each weight fragment is
+// dequantized exactly in registers (G[m] * dec(e) has at most 6 significant
+// bits, so bf16 holds it), the products go through bf16 MFMA with fp32
+// accumulation, and the per-expert fp32 tensor scale is applied once in the
+// epilogue before the round-to-nearest-even conversion to bf16.
 //
 // Work decomposition.  One workgroup (4 waves) computes a kBM x kBN = 128 x 256
-// output tile of one group (expert); each wave owns a 64 x 128 sub-tile of 2 x 4
-// MFMA 32x32x16 tiles, which reads 0.75 KiB of LDS fragments per MFMA (1 KiB at
-// 64 x 64); LDS fragment bandwidth, not the MFMA rate, is what bounds this loop.
+// output tile of one group (expert); wave w owns all 128 rows and columns
+// 64 w .. 64 w + 63 as 4 x 2 MFMA 32x32x16 tiles.  Only the activations go
+// through LDS (each wave reads all of them: 0.5 KiB of LDS per MFMA); the
+// weight codes go straight from memory to the registers of the lanes that feed
+// them to the MFMA and are dequantized there, so no weight value is written to
+// or read from LDS.  Within a K-slice the MFMA's k order is free as long as both
+// operands agree: lane half h = lane / 32 supplies k = 32 h + 8 kk .. + 7 in the
+// kk-th MFMA, which makes a lane's weights for one column 32 consecutive codes
+// (one 16-byte load) and its activations chunk 4 h + kk of the LDS row.
 // The tile list is derived on the device from the group offsets (a wave-wide
 // prefix sum of per-group tile counts), so no host synchronisation is needed.
 // Consecutive workgroup ids are dealt round-robin to the 8 XCDs; the id -> tile
@@ -19,59 +25,61 @@
 // N-tile) order and the N-tiles of one M-tile share their activation rows
 // through that XCD's L2.
 //
-// Pipeline.  The K loop is software-pipelined through registers: the global
-// loads of K-slice s+1 (activations, weight codes, block scales) are issued
-// before the MFMAs of slice s and only written to LDS (activations as is,
-// weights dequantized with gfx950's packed FP4 -> f32 conversion) after them.
-// All operand loads are buffer loads against per-workgroup resources: the
-// per-thread byte offsets are fixed for the whole K loop and the slice position
-// is a scalar offset, so the loop spends no vector instructions on addresses,
-// and rows past the end of A or W read as zeros in hardware (such rows only
-// feed output rows or columns that are never stored).  Only a partial last
-// K-slice (K not a multiple of 64) masks its loads in registers.
+// Block scales.  Per-lane byte loads of scales touch one cache line per lane
+// and cost far more than their size, so when a tile's block scales fit in LDS
+// (K <= 2048, 16-byte aligned rows) they are copied there once per tile with
+// 16-byte loads and read from LDS in the loop; otherwise they are loaded two
+// bytes per lane and slice.
+//
+// Pipeline.  During K-slice t the activations of slice t + 1 and the weight
+// codes of slice t + 2 are in flight (three code register sets rotate); the
+// activations are written to the other of two LDS tiles at the end of the
+// slice, so one barrier per slice suffices.  The fragments of MFMA step kk + 1
+// (weights dequantized, activations read) are produced while the MFMAs of step
+// kk run.  All operand loads are buffer loads against per-workgroup resources:
+// the per-thread byte offsets are fixed for the whole K loop and the slice
+// position is a scalar offset, and rows past the end of A or W read as zeros in
+// hardware (such rows only feed output rows or columns that are never stored).
+// Only a partial first K-slice (K not a multiple of 64) masks its loads.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "tq_device.hpp"
 #include "tq_kernels.hpp"
 
 namespace tq {
 
-#ifndef TQ_GEMM_BN
-#define TQ_GEMM_BN 256
-#endif
-constexpr int kBM = 128, kBN = TQ_GEMM_BN, kBK = 64, kGThreads = 256;
-#ifndef TQ_GEMM_SWZ
-#define TQ_GEMM_SWZ 1
-#endif
-constexpr int kRowPitch = TQ_GEMM_SWZ == 2 ? 144 : 128;  // bytes per LDS row of an operand tile
-constexpr int kATile = kBM * kRowPitch;                  // bf16 activation tile in LDS
-constexpr int kWTile = kBN * kRowPitch;                  // dequantized weight tile in LDS
-constexpr int kSmem = kATile + 2 * kWTile;
-constexpr int kCLd = kBN + 8;                            // bf16 per LDS row of the staged output
-constexpr int kWPieces = kBN / 128;                      // 32-k weight pieces per thread per slice
-constexpr int kNJ = kBN / 64;                            // MFMA tiles per wave along N
-constexpr int kOcc = kBN == 128 ? 3 : 2;                 // workgroups per CU
-static_assert(kBM * kCLd * 2 <= kSmem, "output tile must fit in the operand tiles' LDS");
+constexpr int kBM = 128, kBN = 256, kBK = 64, kGThreads = 256;
+constexpr int kATile = kBM * 128;                 // bf16 activation tile in LDS (128 B rows)
+constexpr int kWSTile = 32768;                    // a tile's weight block scales (kBN rows, K <= 2048)
+constexpr int kASTile = 16384;                    // a tile's activation block scales (kBM rows)
+constexpr int kCLd = kBN + 8;                     // bf16 per LDS row of the staged output
+constexpr int kNI = kBM / 32;                     // MFMA tiles per wave along M
+constexpr int kNJ = 2;                            // MFMA tiles per wave along N (64 columns)
+
+template <bool A_FP4, bool SLDS>
+constexpr int smem_bytes()
+{
+    const int ops = 2 * kATile + (SLDS ? kWSTile + (A_FP4 ? kASTile : 0) : 0);
+    const int out = kBM * kCLd * 2;  // staged output tile, reusing the operand space
+    return ops > out ? ops : out;
+}
 
 // Byte offset of 16-byte chunk j (0..7) of LDS row r.  Rows are 128 bytes; the
 // chunk index is XORed with (r / 2) % 8, so any 16 consecutive rows read at one
 // chunk, and any 2 rows written in full, cover all 16 four-bank groups.
-__device__ __forceinline__ int swz(int r, int j)
-{
-#if TQ_GEMM_SWZ == 2
-    return r * 144 + 16 * j;
-#elif TQ_GEMM_SWZ == 0
-    return r * 128 + 16 * (j ^ (r & 7));
-#else
-    return r * 128 + 16 * (j ^ ((r >> 1) & 7));
-#endif
-}
+__device__ __forceinline__ int swz(int r, int j) { return r * 128 + 16 * (j ^ ((r >> 1) & 7)); }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
+__device__ __forceinline__ uint4 to_uint4(u32x4_t v) { return make_uint4(v[0], v[1], v[2], v[3]); }
 
 // Eight codes (one dword, element 2j in the low nibble of byte j) times the
 // block scale d as four dwords of bf16 pairs.  Exact.
@@ -84,7 +92,7 @@ __device__ __forceinline__ uint4 dequant8_bf16(uint32_t w, float d)
 }
 
 // Activation registers of one slice: bf16 pieces, or (NVFP4 activations) one
-// 32-k piece of one row: codes and two block scales, as for the weights.
+// 32-k piece of one row: codes and, without LDS scales, its two block scales.
 template <bool A_FP4>
 struct ARegs {
     uint4 a[4];   // 4 x 8 bf16 of the A tile
@@ -94,35 +102,34 @@ struct ARegs<true> {
     uint4 w;      // 32 activation codes (one row, 32 consecutive k)
     uint32_t s;   // their two E4M3 block scales (low 16 bits)
 };
+// The weight codes one lane feeds to the MFMAs of one slice: for each of its
+// kNJ columns, 32 consecutive k (its half of the slice), and, without LDS
+// scales, their two block scales.
 struct WRegs {
-    uint4 w[kWPieces];     // per piece: 32 weight codes (one row, 32 consecutive k)
-    uint32_t s[kWPieces];  // per piece: its two E4M3 block scales (low 16 bits)
+    uint4 w[kNJ];
+    uint32_t s[kNJ];
 };
-
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint4 to_uint4(u32x4_t v) { return make_uint4(v[0], v[1], v[2], v[3]); }
 
 // A_FP4 = false: `a` is bf16 [m_total][k].  A_FP4 = true: `a` holds NVFP4 codes
 // [m_total][k/2] with block scales `a_scales` [m_total][k/16] and the single
 // tensor scale a_tensor_scale[0]; the activation tile is dequantized exactly into
-// LDS like the weights.
-template <bool A_FP4>
-__global__ __launch_bounds__(kGThreads, kOcc) void grouped_gemm_nvfp4_kernel(
+// LDS.  SLDS: block scales are staged in LDS per tile (see the launcher for the
+// conditions).
+template <bool A_FP4, bool SLDS>
+__global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
     const void* __restrict__ a, const uint8_t* __restrict__ a_scales,
     const float* __restrict__ a_tensor_scale, const int32_t* __restrict__ group_offsets,
     int num_groups, int64_t m_total, int64_t n, int64_t k, const uint8_t* __restrict__ w_codes,
     const uint8_t* __restrict__ w_scales, const float* __restrict__ w_tensor_scale,
     uint16_t* __restrict__ out, int n_tiles)
 {
-    // A tile, then two dequantized W tiles (the one being read, the one being filled).
-    // The tile id is passed through the start of the second W tile, which is first
-    // written after the prologue's barrier.
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmem];
-    int64_t* s_tile = reinterpret_cast<int64_t*>(smem + kATile + kWTile);
-    uint8_t* As = smem;
+    // Two activation tiles (the one being read, the one being filled), then the
+    // staged scales.  The tile id is passed through the start of the second
+    // activation tile, which is first written after the prologue's barriers.
+    __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<A_FP4, SLDS>()];
+    int64_t* s_tile = reinterpret_cast<int64_t*>(smem + kATile);
+    uint8_t* const Ws = smem + 2 * kATile;            // weight scales [kBN][K/16]
+    uint8_t* const As_s = smem + 2 * kATile + kWSTile;  // activation scales [kBM][K/16]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -189,31 +196,38 @@ __global__ __launch_bounds__(kGThreads, kOcc) void grouped_gemm_nvfp4_kernel(
         }
     }
     __syncthreads();
-    const int64_t e = s_tile[0];
+    // The tile's coordinates are the same in every lane: keep them in scalar
+    // registers so that every branch on them below is a scalar branch.
+    auto uniform64 = [](int64_t v) -> int64_t {
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+        return (int64_t)(((uint64_t)hi << 32) | lo);
+    };
+    const int64_t e = uniform64(s_tile[0]);
     if (e < 0)
         return;
-    const int64_t row0 = (int64_t)group_offsets[e] + s_tile[1] * kBM;
-    const int64_t row_end = group_offsets[e + 1];
-    const int64_t col0 = s_tile[2] * kBN;
-    const int64_t kb = k / 16;  // scale blocks per weight row
+    const int64_t row0 = uniform64((int64_t)group_offsets[e] + s_tile[1] * kBM);
+    const int64_t row_end = uniform64(group_offsets[e + 1]);
+    const int64_t col0 = uniform64(s_tile[2] * kBN);
+    const int kb = (int)(k / 16);  // scale blocks per row
+    const int kh = (int)(k / 2);   // code bytes per NVFP4 row
 
-    // per-workgroup buffer resources over the tile's rows of A and W (and W's
+    // per-workgroup buffer resources over the tile's rows of A and W (and their
     // scales); loads past num_records return zeros
-    const int64_t a_rows = m_total - row0 < kBM ? m_total - row0 : kBM;
-    const int64_t w_rows = n - col0 < kBN ? n - col0 : kBN;
+    const int a_rows = (int)(m_total - row0 < kBM ? m_total - row0 : kBM);
+    const int w_rows = (int)(n - col0 < kBN ? n - col0 : kBN);
     const __amdgpu_buffer_rsrc_t rs_a = A_FP4
-        ? __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)a + row0 * (k / 2)), 0,
-                                            (int)(a_rows * (k / 2)), 0x00020000)
+        ? __builtin_amdgcn_make_buffer_rsrc((void*)((const uint8_t*)a + row0 * kh), 0,
+                                            a_rows * kh, 0x00020000)
         : __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)a + row0 * k), 0,
-                                            (int)(a_rows * k * 2), 0x00020000);
+                                            a_rows * (int)k * 2, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_as = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(A_FP4 ? a_scales + row0 * kb : w_scales), 0, A_FP4 ? (int)(a_rows * kb) : 0,
-        0x00020000);
+        (void*)(A_FP4 ? a_scales + row0 * kb : w_scales), 0, A_FP4 ? a_rows * kb : 0, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(w_codes + (e * n + col0) * (k / 2)), 0, (int)(w_rows * (k / 2)), 0x00020000);
+        (void*)(w_codes + (e * n + col0) * kh), 0, w_rows * kh, 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_s = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(w_scales + (e * n + col0) * kb), 0, (int)(w_rows * kb), 0x00020000);
-    // per-thread byte offsets: A pieces (row r, 8 k at c8), one weight row half
+        (void*)(w_scales + (e * n + col0) * kb), 0, w_rows * kb, 0x00020000);
+    // per-thread byte offsets: bf16 activation pieces (row r, 8 k at c8)
     int voff_a[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
@@ -222,56 +236,58 @@ __global__ __launch_bounds__(kGThreads, kOcc) void grouped_gemm_nvfp4_kernel(
     }
     // NVFP4 activations: one 32-k piece per thread, row tid / 2, k half tid % 2
     const int an_row = tid >> 1;
-    const int voff_ac = an_row * (int)(k / 2) + 16 * (tid & 1);
-    const int voff_as = an_row * (int)kb + 2 * (tid & 1);
-    // weight pieces: piece q = tid + 256 p covers row q / 2, k half q % 2 of the slice
-    int wn_row[kWPieces], voff_w[kWPieces], voff_s[kWPieces];
-    const int wk_half = tid & 1;
+    const int voff_ac = an_row * kh + 16 * (tid & 1);
+    const int voff_as = an_row * kb + 2 * (tid & 1);
+    // weights: this lane's column of each of its two 32-column MFMA tiles, k half h
+    const int h = lane >> 5;
+    int wcol[kNJ], voff_w[kNJ], voff_s[kNJ];
 #pragma unroll
-    for (int p = 0; p < kWPieces; ++p) {
-        wn_row[p] = (tid + kGThreads * p) >> 1;
-        voff_w[p] = wn_row[p] * (int)(k / 2) + 16 * wk_half;
-        voff_s[p] = wn_row[p] * (int)kb + 2 * wk_half;
+    for (int j = 0; j < kNJ; ++j) {
+        wcol[j] = 64 * wave + 32 * j + (lane & 31);
+        voff_w[j] = wcol[j] * kh + 16 * h;
+        voff_s[j] = wcol[j] * kb + 2 * h;
     }
 
     // K-slices: when K is not a multiple of 64 the partial slice [0, K % 64) comes
     // first and is loaded (masked) before the loop; every slice the loop loads is
     // full, so the loop issues the same loads every time, and a slice past the
     // end is loaded with an out-of-range scalar offset, which reads zeros.
-    const int64_t r_tail = k % kBK;
-    const int64_t steps = k / kBK + (r_tail ? 1 : 0);
-    auto kofs = [&](int64_t t) -> int64_t {
-        return r_tail ? (t == 0 ? 0 : r_tail + kBK * (t - 1)) : kBK * t;
-    };
+    const int r_tail = (int)(k % kBK);
+    const int steps = (int)(k / kBK) + (r_tail ? 1 : 0);
+    const int k_shift = r_tail ? kBK - r_tail : 0;  // slice t >= 1 starts at 64 t - k_shift
+    auto kofs = [&](int t) -> int { return t == 0 ? 0 : kBK * t - k_shift; };
     constexpr int kOutOfRange = 0x7FFFFF00;  // + any per-thread offset: beyond num_records
-    auto load_a = [&](int64_t t, ARegs<A_FP4>& R) {
+    auto load_a = [&](int t, ARegs<A_FP4>& R) {
         if constexpr (A_FP4) {
             const bool ok = t < steps;
-            const int so_c = ok ? (int)(kofs(t) / 2) : kOutOfRange;
-            const int so_s = ok ? (int)(kofs(t) / 16) : kOutOfRange;
-            R.w = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs_a, voff_ac, so_c, 0));
-            R.s = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_as, voff_as, so_s, 0) |
-                  ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_as, voff_as + 1, so_s, 0) << 8);
+            R.w = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs_a, voff_ac, ok ? kofs(t) / 2 : kOutOfRange, 0));
+            if constexpr (!SLDS) {
+                const int so_s = ok ? kofs(t) / 16 : kOutOfRange;
+                R.s = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_as, voff_as, so_s, 0) |
+                      ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_as, voff_as + 1, so_s, 0) << 8);
+            }
         } else {
-            const int so = t < steps ? (int)(kofs(t) * 2) : kOutOfRange;
+            const int so = t < steps ? kofs(t) * 2 : kOutOfRange;
 #pragma unroll
             for (int it = 0; it < 4; ++it)
                 R.a[it] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs_a, voff_a[it], so, 0));
         }
     };
-    auto load_w = [&](int64_t t, WRegs& R) {
+    auto load_w = [&](int t, WRegs& R) {
         const bool ok = t < steps;
-        const int so_w = ok ? (int)(kofs(t) / 2) : kOutOfRange;
-        const int so_s = ok ? (int)(kofs(t) / 16) : kOutOfRange;
+        const int so_w = ok ? kofs(t) / 2 : kOutOfRange;
+        const int so_s = ok ? kofs(t) / 16 : kOutOfRange;
 #pragma unroll
-        for (int p = 0; p < kWPieces; ++p) {
-            R.w[p] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs_w, voff_w[p], so_w, 0));
-            R.s[p] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_s, voff_s[p], so_s, 0) |
-                     ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_s, voff_s[p] + 1, so_s, 0) << 8);
+        for (int j = 0; j < kNJ; ++j) {
+            R.w[j] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs_w, voff_w[j], so_w, 0));
+            if constexpr (!SLDS)
+                R.s[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_s, voff_s[j], so_s, 0) |
+                         ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_s, voff_s[j] + 1, so_s, 0) << 8);
         }
     };
-    // the partial first slice: activations at or beyond K % 64 are zeroed, weights
-    // are loaded block by block (a 16-byte load could run past the row)
+    // The partial first slice: codes at or beyond K % 64 are zeroed and loaded
+    // block by block (a 16-byte load could run past the row); so are bf16
+    // activations.  Scales of blocks past K % 64 are zeroed where they are used.
     auto load_partial = [&](ARegs<A_FP4>& RA_, WRegs& RW_) {
         if constexpr (A_FP4) {
             RA_.w = make_uint4(0, 0, 0, 0);
@@ -280,13 +296,15 @@ __global__ __launch_bounds__(kGThreads, kOcc) void grouped_gemm_nvfp4_kernel(
                 const u32x2_t lo = __builtin_amdgcn_raw_buffer_load_b64(rs_a, voff_ac, 0, 0);
                 RA_.w.x = lo[0];
                 RA_.w.y = lo[1];
-                RA_.s = __builtin_amdgcn_raw_buffer_load_b8(rs_as, voff_as, 0, 0);
+                if constexpr (!SLDS)
+                    RA_.s = __builtin_amdgcn_raw_buffer_load_b8(rs_as, voff_as, 0, 0);
             }
             if (32 * (tid & 1) + 16 < r_tail) {
                 const u32x2_t hi = __builtin_amdgcn_raw_buffer_load_b64(rs_a, voff_ac + 8, 0, 0);
                 RA_.w.z = hi[0];
                 RA_.w.w = hi[1];
-                RA_.s |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_as, voff_as + 1, 0, 0) << 8;
+                if constexpr (!SLDS)
+                    RA_.s |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_as, voff_as + 1, 0, 0) << 8;
             }
         } else {
 #pragma unroll
@@ -297,32 +315,70 @@ __global__ __launch_bounds__(kGThreads, kOcc) void grouped_gemm_nvfp4_kernel(
             }
         }
 #pragma unroll
-        for (int p = 0; p < kWPieces; ++p) {
-            RW_.w[p] = make_uint4(0, 0, 0, 0);
-            RW_.s[p] = 0;
-            if (32 * wk_half < r_tail) {
-                const u32x2_t lo = __builtin_amdgcn_raw_buffer_load_b64(rs_w, voff_w[p], 0, 0);
-                RW_.w[p].x = lo[0];
-                RW_.w[p].y = lo[1];
-                RW_.s[p] = __builtin_amdgcn_raw_buffer_load_b8(rs_s, voff_s[p], 0, 0);
+        for (int j = 0; j < kNJ; ++j) {
+            RW_.w[j] = make_uint4(0, 0, 0, 0);
+            RW_.s[j] = 0;
+            if (32 * h < r_tail) {
+                const u32x2_t lo = __builtin_amdgcn_raw_buffer_load_b64(rs_w, voff_w[j], 0, 0);
+                RW_.w[j].x = lo[0];
+                RW_.w[j].y = lo[1];
+                if constexpr (!SLDS)
+                    RW_.s[j] = __builtin_amdgcn_raw_buffer_load_b8(rs_s, voff_s[j], 0, 0);
             }
-            if (32 * wk_half + 16 < r_tail) {
-                const u32x2_t hi = __builtin_amdgcn_raw_buffer_load_b64(rs_w, voff_w[p] + 8, 0, 0);
-                RW_.w[p].z = hi[0];
-                RW_.w[p].w = hi[1];
-                RW_.s[p] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_s, voff_s[p] + 1, 0, 0) << 8;
+            if (32 * h + 16 < r_tail) {
+                const u32x2_t hi = __builtin_amdgcn_raw_buffer_load_b64(rs_w, voff_w[j] + 8, 0, 0);
+                RW_.w[j].z = hi[0];
+                RW_.w[j].w = hi[1];
+                if constexpr (!SLDS)
+                    RW_.s[j] |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_s, voff_s[j] + 1, 0, 0) << 8;
             }
         }
     };
-    auto store_a = [&](const ARegs<A_FP4>& R) {
+    // SLDS: copy the tile's block scales (rows x K/16 bytes, contiguous and
+    // 16-byte aligned) into LDS with 16-byte loads; loads past the tile's rows
+    // read zeros.
+    auto copy_scales = [&](__amdgpu_buffer_rsrc_t rs, int bytes, uint8_t* dst, auto cap) __attribute__((always_inline)) {
+        constexpr int kRounds = decltype(cap)::value / (16 * kGThreads);
+        uint4 v[kRounds];
+#pragma unroll
+        for (int u = 0; u < kRounds; ++u)
+            if (u * 16 * kGThreads < bytes)
+                v[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs, 16 * (tid + kGThreads * u), 0, 0));
+#pragma unroll
+        for (int u = 0; u < kRounds; ++u)
+            if (u * 16 * kGThreads < bytes)
+                *reinterpret_cast<uint4*>(dst + 16 * (tid + kGThreads * u)) = v[u];
+    };
+    // two scale bytes (blocks 2 q, 2 q + 1 of a 32-k piece) of slice t from a staged row
+    auto lds_scales = [&](const uint8_t* rowp, int t, int q) -> uint32_t {
+        const uint8_t* p = rowp + kofs(t) / 16 + 2 * q;
+        return (uint32_t)p[0] | ((uint32_t)p[1] << 8);
+    };
+    // blocks of a partial first slice past K % 64 get zero scales
+    auto mask_partial = [&](uint32_t s, int q) -> uint32_t {
+        if (32 * q >= r_tail)
+            s &= 0xFF00u;
+        if (32 * q + 16 >= r_tail)
+            s &= 0x00FFu;
+        return s;
+    };
+    // activations of slice t into LDS tile As (NVFP4 ones dequantized exactly)
+    auto store_a = [&](const ARegs<A_FP4>& R, int t, uint8_t* As) {
         if constexpr (A_FP4) {
-            const f32x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(R.s, 1.0f, false);
+            uint32_t s = R.s;
+            if constexpr (SLDS) {
+                s = lds_scales(As_s + an_row * kb, t < steps ? t : steps - 1, tid & 1);
+                if (t == 0 && r_tail)
+                    s = mask_partial(s, tid & 1);
+            }
+            const f32x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(s, 1.0f, false);
             const int j0 = 4 * (tid & 1);
             *reinterpret_cast<uint4*>(As + swz(an_row, j0 + 0)) = dequant8_bf16(R.w.x, d[0]);
             *reinterpret_cast<uint4*>(As + swz(an_row, j0 + 1)) = dequant8_bf16(R.w.y, d[0]);
             *reinterpret_cast<uint4*>(As + swz(an_row, j0 + 2)) = dequant8_bf16(R.w.z, d[1]);
             *reinterpret_cast<uint4*>(As + swz(an_row, j0 + 3)) = dequant8_bf16(R.w.w, d[1]);
         } else {
+            (void)t;
 #pragma unroll
             for (int it = 0; it < 4; ++it) {
                 const int idx = tid + it * kGThreads;
@@ -330,90 +386,122 @@ __global__ __launch_bounds__(kGThreads, kOcc) void grouped_gemm_nvfp4_kernel(
             }
         }
     };
-    // one quarter (8 codes) of weight piece p, dequantized into buffer Wd
-    auto dequant_quarter = [&](const WRegs& R, int p, int q, uint8_t* Wd) {
-        const f32x2_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(R.s[p], 1.0f, false);
-        const uint32_t w = q == 0 ? R.w[p].x : (q == 1 ? R.w[p].y : (q == 2 ? R.w[p].z : R.w[p].w));
-        *reinterpret_cast<uint4*>(Wd + swz(wn_row[p], 4 * wk_half + q)) =
-            dequant8_bf16(w, q < 2 ? d[0] : d[1]);
-    };
 
-    const int wm = wave >> 1, wn = wave & 1;
-    const bool live[2] = {row0 + 64 * wm < row_end, row0 + 64 * wm + 32 < row_end};
-    f32x16_t acc[2][kNJ];
+    f32x16_t acc[kNI][kNJ];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kNI; ++i)
 #pragma unroll
         for (int j = 0; j < kNJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
                 acc[i][j][r] = 0.0f;
 
-    // Slice t reads A from As and W from buffer t % 2.  During slice t the
-    // activations of t + 1 and the weight codes of t + 2 are in flight, and the
-    // codes of t + 1 (loaded one slice earlier) are dequantized into the other W
-    // buffer between the MFMAs.
     ARegs<A_FP4> RA;
-    WRegs RW, RW2 = {};
+    WRegs S0, S1, S2 = {};
+    uint32_t sc[kNJ] = {};  // SLDS: weight scale bytes of the slice about to run
     if (steps > 0) {
         if (r_tail) {
-            load_partial(RA, RW);
+            load_partial(RA, S0);
         } else {
             load_a(0, RA);
-            load_w(0, RW);
+            load_w(0, S0);
         }
-        store_a(RA);
-#pragma unroll
-        for (int p = 0; p < kWPieces; ++p)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                dequant_quarter(RW, p, q, smem + kATile);
-        load_w(1, RW);
+        load_w(1, S1);
+        if constexpr (SLDS) {
+            copy_scales(rs_s, w_rows * kb, Ws, std::integral_constant<int, kWSTile>{});
+            if constexpr (A_FP4) {
+                copy_scales(rs_as, a_rows * kb, As_s, std::integral_constant<int, kASTile>{});
+                __syncthreads();  // store_a reads activation scales other threads copied
+            }
+        }
+        store_a(RA, 0, smem);
     }
     __syncthreads();
-    // one K-slice; `cur` holds the codes of slice t + 1, `nxt` receives those of t + 2
-    auto step = [&](int64_t t, const WRegs& cur, WRegs& nxt) {
-        const bool more = t + 1 < steps;
+    if constexpr (SLDS) {
+        if (steps > 0) {
+#pragma unroll
+            for (int j = 0; j < kNJ; ++j) {
+                sc[j] = lds_scales(Ws + wcol[j] * kb, 0, h);
+                if (r_tail)
+                    sc[j] = mask_partial(sc[j], h);
+            }
+        }
+    }
+    // One slice with NL live 32-row blocks (blocks past the group's end only feed
+    // rows that are never stored, so their MFMAs are skipped).  `cur` holds the
+    // codes of slice t, `nxt` receives those of t + 2.
+    auto step = [&](auto nl, int t, const WRegs& cur, WRegs& nxt) __attribute__((always_inline)) {
+        constexpr int NL = decltype(nl)::value;
         load_a(t + 1, RA);
         load_w(t + 2, nxt);
-        const uint8_t* Wc = smem + kATile + kWTile * (int)(t & 1);
-        uint8_t* Wn = smem + kATile + kWTile * (1 - (int)(t & 1));
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads at the top of the slice
+        const uint8_t* Ac = smem + kATile * (t & 1);
+        f32x2_t d[kNJ];
 #pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-            const int ch = 2 * kk + (lane >> 5);
-            bf16x8_t af[2], bfr[kNJ];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                af[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                    As + swz(64 * wm + 32 * i + (lane & 31), ch)));
+        for (int j = 0; j < kNJ; ++j)
+            d[j] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(SLDS ? sc[j] : cur.s[j], 1.0f, false);
+        if constexpr (SLDS) {
+            // next slice's weight scales (past the last slice: of no consequence)
 #pragma unroll
             for (int j = 0; j < kNJ; ++j)
-                bfr[j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                    Wc + swz((kBN / 2) * wn + 32 * j + (lane & 31), ch)));
-            if (more) {
+                sc[j] = lds_scales(Ws + wcol[j] * kb, t + 1 < steps ? t + 1 : t, h);
+        }
+        auto word = [&](int j, int kk) -> uint32_t {
+            return kk == 0 ? cur.w[j].x : (kk == 1 ? cur.w[j].y : (kk == 2 ? cur.w[j].z : cur.w[j].w));
+        };
+        auto afrag = [&](int i, int kk) -> bf16x8_t {
+            return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
+                Ac + swz(32 * i + (lane & 31), 4 * h + kk)));
+        };
+        bf16x8_t bf[2][kNJ], af[2][kNI];
 #pragma unroll
-                for (int p = 0; p < kWPieces; ++p)
-                    dequant_quarter(cur, p, kk, Wn);
+        for (int j = 0; j < kNJ; ++j)
+            bf[0][j] = __builtin_bit_cast(bf16x8_t, dequant8_bf16(word(j, 0), d[j][0]));
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+            af[0][i] = afrag(i, 0);
+#pragma unroll
+        for (int kk = 0; kk < kBK / 16; ++kk) {
+            const int c = kk & 1, nx = c ^ 1;
+            if (kk + 1 < kBK / 16) {
+#pragma unroll
+                for (int i = 0; i < NL; ++i)
+                    af[nx][i] = afrag(i, kk + 1);
+#pragma unroll
+                for (int j = 0; j < kNJ; ++j)
+                    bf[nx][j] = __builtin_bit_cast(
+                        bf16x8_t, dequant8_bf16(word(j, kk + 1), d[j][(kk + 1) >> 1]));
             }
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-                if (live[i])  // 32-row blocks past the group's end only feed unstored rows
+            for (int i = 0; i < NL; ++i)
 #pragma unroll
-                    for (int j = 0; j < kNJ; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                for (int j = 0; j < kNJ; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bf[c][j], acc[i][j], 0, 0, 0);
         }
+        // activations of slice t + 1 into the other tile (zeros past the last
+        // slice, into a tile nobody reads again)
+        store_a(RA, t + 1, smem + kATile * (1 - (t & 1)));
         __syncthreads();
-        if (more) {
-            store_a(RA);
-            __syncthreads();
+    };
+    // three slices per trip so that the three code register sets rotate without copies
+    auto run = [&](auto nl) __attribute__((always_inline)) {
+        for (int t = 0; t < steps; t += 3) {
+            step(nl, t, S0, S2);
+            if (t + 1 < steps)
+                step(nl, t + 1, S1, S0);
+            if (t + 2 < steps)
+                step(nl, t + 2, S2, S1);
         }
     };
-    // two slices per trip so that the two code registers swap roles without copies
-    for (int64_t t = 0; t < steps; t += 2) {
-        step(t, RW, RW2);
-        if (t + 1 < steps)
-            step(t + 1, RW2, RW);
-    }
+    const int64_t live_rows = row_end - row0;
+    if (live_rows > 96)
+        run(std::integral_constant<int, 4>{});
+    else if (live_rows > 64)
+        run(std::integral_constant<int, 3>{});
+    else if (live_rows > 32)
+        run(std::integral_constant<int, 2>{});
+    else
+        run(std::integral_constant<int, 1>{});
 
     // ---- epilogue: scale, RNE to bf16, stage the tile in LDS, coalesced stores ----
     const float s_e = A_FP4 ? w_tensor_scale[e] * a_tensor_scale[0] : w_tensor_scale[e];
@@ -425,7 +513,7 @@ __global__ __launch_bounds__(kGThreads, kOcc) void grouped_gemm_nvfp4_kernel(
     uint32_t* Cw = reinterpret_cast<uint32_t*>(smem);
     const bool odd = lane & 1;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kNI; ++i)
 #pragma unroll
         for (int j = 0; j < kNJ; ++j)
 #pragma unroll
@@ -436,8 +524,8 @@ __global__ __launch_bounds__(kGThreads, kOcc) void grouped_gemm_nvfp4_kernel(
                     __builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
                 const f32x2_t pair = {odd ? recv : v0, odd ? v1 : recv};
                 const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(pair, bf16x2_t));
-                const int row = 64 * wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) + (odd ? 1 : 0);
-                const int col = (kBN / 2) * wn + 32 * j + (lane & 31) - (odd ? 1 : 0);
+                const int row = 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) + (odd ? 1 : 0);
+                const int col = 64 * wave + 32 * j + (lane & 31) - (odd ? 1 : 0);
                 Cw[(row * kCLd + col) >> 1] = w;
             }
     __syncthreads();
@@ -474,9 +562,22 @@ static void launch_gemm(const void* a, const uint8_t* a_scales, const float* a_t
         return;
     // a multiple of 8 with at least ceil(total/8) groups per XCD slot
     grid = ((grid + 7) / 8) * 8;
-    hipLaunchKernelGGL(grouped_gemm_nvfp4_kernel<A_FP4>, dim3((unsigned)grid), dim3(kGThreads), 0,
-                       s, a, a_scales, a_tensor_scale, group_offsets, num_groups, m_total, n, k,
-                       w_codes, w_scales, w_tensor_scale, out, n_tiles);
+    // Scales staged in LDS: a tile's block of scales must fit and start on a
+    // 16-byte boundary.  Weight tiles start at row e * n + 256 c; activation
+    // tiles at any row, so their rows must be whole 16-byte units.
+    const int64_t kb = k / 16;
+    auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+    bool slds = kb * kBN <= kWSTile && al16(w_scales) && (n * kb) % 16 == 0;
+    if (A_FP4)
+        slds = slds && kb * kBM <= kASTile && al16(a_scales) && kb % 16 == 0;
+    if (slds)
+        hipLaunchKernelGGL((grouped_gemm_nvfp4_kernel<A_FP4, true>), dim3((unsigned)grid),
+                           dim3(kGThreads), 0, s, a, a_scales, a_tensor_scale, group_offsets,
+                           num_groups, m_total, n, k, w_codes, w_scales, w_tensor_scale, out, n_tiles);
+    else
+        hipLaunchKernelGGL((grouped_gemm_nvfp4_kernel<A_FP4, false>), dim3((unsigned)grid),
+                           dim3(kGThreads), 0, s, a, a_scales, a_tensor_scale, group_offsets,
+                           num_groups, m_total, n, k, w_codes, w_scales, w_tensor_scale, out, n_tiles);
 }
 
 void launch_grouped_gemm_nvfp4(const uint16_t* a, const int32_t* group_offsets, int num_groups,

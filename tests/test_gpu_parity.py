@@ -612,6 +612,7 @@ def test_grouped_gemm_forward_shape():
 GEMM_EDGES = [
     ([5, 0, 7, 1], 64, 64), ([1], 2, 16), ([130, 3], 66, 80), ([0, 0, 257], 200, 48),
     ([128, 128], 128, 128), ([64] * 5, 256, 2064), ([1, 2, 3, 4, 5, 6, 7], 130, 32),
+    ([40, 300], 256, 1040), ([77], 128, 112),
 ]
 
 
