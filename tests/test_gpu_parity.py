@@ -399,8 +399,8 @@ def test_mxfp8_quantize_activations_full_size():
     rng = np.random.default_rng(2)
     rows = np.unique(np.concatenate([[0, 1, T - 1], rng.choice(T, 512, replace=False)]))
     o = oracle.quantize_mxfp8(xr.cpu()[rows], 1, rows.size, Hd)
-    assert np.array_equal(npu8(q.codes)[rows].reshape(-1), o["codes"])
-    assert np.array_equal(npu8(q.scales)[rows].reshape(-1), o["scales"])
+    assert np.array_equal(npu8(q.codes).reshape(T, Hd)[rows].reshape(-1), o["codes"])
+    assert np.array_equal(npu8(q.scales).reshape(T, Hd // 32)[rows].reshape(-1), o["scales"])
 
 
 MX_SR_SHAPES = [(1, 32, 16), (1, 64, 80), (3, 288, 96), (2, 32, 1040), (1, 1024, 1024)]
