@@ -110,66 +110,69 @@ def main():
     QR, QN, QG = q_bufs(), q_bufs(), q_bufs()
     nh = max(nl - first_hint, 0)
     H = torch.empty((max(nh, 1), ops.hint_words(n_layer)), dtype=torch.int32, device=dev)
-    CNT = torch.empty((nl, 2, EXPERTS, 2), dtype=torch.int64, device=dev)
+    CNT = torch.empty((2, nl, EXPERTS, 2), dtype=torch.int64, device=dev)  # [nearest|guided]
     QT = ops.NVFP4(torch.empty((nl, EXPERTS, COLS, ROWS // 2), dtype=torch.uint8, device=dev),
                    torch.empty((nl, EXPERTS, COLS, ROWS // 16), dtype=torch.uint8, device=dev),
                    torch.empty((nl, EXPERTS), dtype=torch.float32, device=dev), None)
     OUT = torch.empty((nl, TOKENS, ROWS), dtype=torch.bfloat16, device=dev)
 
     # ---------------- pre-bound calls (validated once by the library) ----------------
-    # The step runs as phases, each one kernel over all layers: the rollout's
-    # amax and quantize (with hints for the latter half), the trainer's amax,
-    # nearest and guided quantize, the mismatch counts, the SR transpose and the
-    # grouped GEMM.  Events bracket each phase (one kernel, back to back), so the
+    # The step runs as phases, each one kind of kernel: the rollout's amax and
+    # quantize (with hints for the latter half), the trainer's amax, nearest and
+    # guided quantize, the mismatch counts, the SR transpose and the grouped GEMM.
+    # The layers' tensors are contiguous, so the streaming phases cover all the
+    # layers they apply to in one call (a batch of layers x experts tensors);
+    # the grouped GEMM runs once per layer.  Events bracket each phase, so the
     # per-kernel averages carry no per-call event overhead.
-    phases = {}  # phase name -> list of (category, fn, args)
+    phases = {}  # phase name -> list of (category, fn, args, layers covered)
 
-    def add(phase, cat, fn, a):
-        phases.setdefault(phase, []).append((cat, fn, a))
+    def add(phase, cat, fn, a, layers):
+        phases.setdefault(phase, []).append((cat, fn, a, layers))
 
-    for l in range(nl):
-        hinted = l >= first_hint
-        hl = H[l - first_hint] if hinted else None
-        add("amax_rollout", "amax", L.tq_tensor_amax,
-            (P(XR[l]), TQ_BF16, EXPERTS, per, P(QR.tensor_amax[l]), sp))
-    for l in range(nl):
-        hinted = l >= first_hint
-        hl = H[l - first_hint] if hinted else None
-        add("quantize_hint_rollout" if hinted else "quantize_rollout",
-            "quantize_hint" if hinted else "quantize", L.tq_quantize,
-            (P(XR[l]), TQ_BF16, EXPERTS, ROWS, COLS, P(QR.tensor_amax[l]), P(QR.codes[l]),
-             P(QR.scales[l]), P(QR.tensor_scale[l]), P(hl), TQ_AMAX_GIVEN, sp))
-    for l in range(nl):
-        add("amax_trainer", "amax", L.tq_tensor_amax,
-            (P(XT[l]), TQ_BF16, EXPERTS, per, P(QN.tensor_amax[l]), sp))
-    for l in range(nl):
-        add("quantize_trainer", "quantize", L.tq_quantize,
-            (P(XT[l]), TQ_BF16, EXPERTS, ROWS, COLS, P(QN.tensor_amax[l]), P(QN.codes[l]),
-             P(QN.scales[l]), P(QN.tensor_scale[l]), None, TQ_AMAX_GIVEN, sp))
-    for l in range(first_hint, nl):
+    fh, E = first_hint, EXPERTS
+    add("amax_rollout", "amax", L.tq_tensor_amax,
+        (P(XR), TQ_BF16, nl * E, per, P(QR.tensor_amax), sp), nl)
+    if fh > 0:
+        add("quantize_rollout", "quantize", L.tq_quantize,
+            (P(XR[0]), TQ_BF16, fh * E, ROWS, COLS, P(QR.tensor_amax[0]), P(QR.codes[0]),
+             P(QR.scales[0]), P(QR.tensor_scale[0]), None, TQ_AMAX_GIVEN, sp), fh)
+    if nh > 0:
+        add("quantize_hint_rollout", "quantize_hint", L.tq_quantize,
+            (P(XR[fh]), TQ_BF16, nh * E, ROWS, COLS, P(QR.tensor_amax[fh]), P(QR.codes[fh]),
+             P(QR.scales[fh]), P(QR.tensor_scale[fh]), P(H), TQ_AMAX_GIVEN, sp), nh)
+    add("amax_trainer", "amax", L.tq_tensor_amax,
+        (P(XT), TQ_BF16, nl * E, per, P(QN.tensor_amax), sp), nl)
+    add("quantize_trainer", "quantize", L.tq_quantize,
+        (P(XT), TQ_BF16, nl * E, ROWS, COLS, P(QN.tensor_amax), P(QN.codes), P(QN.scales),
+         P(QN.tensor_scale), None, TQ_AMAX_GIVEN, sp), nl)
+    if nh > 0:
         add("guided_trainer", "guided", L.tq_quantize_guided,
-            (P(XT[l]), TQ_BF16, EXPERTS, ROWS, COLS, P(QN.tensor_amax[l]), P(H[l - first_hint]),
-             P(QG.codes[l]), P(QG.scales[l]), P(QG.tensor_scale[l]), TQ_AMAX_GIVEN, sp))
-    for l in range(nl):
+            (P(XT[fh]), TQ_BF16, nh * E, ROWS, COLS, P(QN.tensor_amax[fh]), P(H),
+             P(QG.codes[fh]), P(QG.scales[fh]), P(QG.tensor_scale[fh]), TQ_AMAX_GIVEN, sp), nh)
+    add("mismatch", "mismatch", L.tq_code_mismatch,
+        (P(QR.codes), P(QN.codes), nl * E, per, P(CNT[0]), sp), nl)
+    if nh > 0:
         add("mismatch", "mismatch", L.tq_code_mismatch,
-            (P(QR.codes[l]), P(QN.codes[l]), EXPERTS, per, P(CNT[l, 0]), sp))
-        if l >= first_hint:
-            add("mismatch", "mismatch", L.tq_code_mismatch,
-                (P(QR.codes[l]), P(QG.codes[l]), EXPERTS, per, P(CNT[l, 1]), sp))
-    for l in range(nl):
-        trainer = QG if l >= first_hint else QN
+            (P(QR.codes[fh]), P(QG.codes[fh]), nh * E, per, P(CNT[1, fh]), sp), nh)
+    # the backward copy of the trainer's weights: unguided layers from QN, hinted
+    # ones from QG (Philox seed 0 and 1; the counter runs over each call's elements)
+    if fh > 0:
         add("sr_transpose", "sr_transpose", L.tq_requant_transpose_sr,
-            (P(trainer.codes[l]), P(trainer.scales[l]), P(trainer.tensor_scale[l]), EXPERTS,
-             ROWS, COLS, C.c_uint64(l), P(QT.codes[l]), P(QT.scales[l]), P(QT.tensor_scale[l]), sp))
+            (P(QN.codes[0]), P(QN.scales[0]), P(QN.tensor_scale[0]), fh * E, ROWS, COLS,
+             C.c_uint64(0), P(QT.codes[0]), P(QT.scales[0]), P(QT.tensor_scale[0]), sp), fh)
+    if nh > 0:
+        add("sr_transpose", "sr_transpose", L.tq_requant_transpose_sr,
+            (P(QG.codes[fh]), P(QG.scales[fh]), P(QG.tensor_scale[fh]), nh * E, ROWS, COLS,
+             C.c_uint64(1), P(QT.codes[fh]), P(QT.scales[fh]), P(QT.tensor_scale[fh]), sp), nh)
     for l in range(nl):
-        trainer = QG if l >= first_hint else QN
+        trainer = QG if l >= fh else QN
         add("gemm", "gemm", L.tq_grouped_gemm_nvfp4,
             (P(A[l]), P(OFF), EXPERTS, TOKENS, ROWS, COLS, P(trainer.codes[l]),
-             P(trainer.scales[l]), P(trainer.tensor_scale[l]), P(OUT[l]), sp))
+             P(trainer.scales[l]), P(trainer.tensor_scale[l]), P(OUT[l]), sp), 1)
     calls = [c for ph in phases.values() for c in ph]
 
-    # algorithmic bytes per call (inputs read once + outputs written once)
-    def call_bytes(cat):
+    # algorithmic bytes per layer covered (inputs read once + outputs written once)
+    def layer_bytes(cat):
         n = n_layer
         return {
             "amax": 2.0 * n,
@@ -181,14 +184,14 @@ def main():
             "gemm": TOKENS * COLS * 2 + n * (0.5 + 1 / 16) + TOKENS * ROWS * 2,
         }[cat]
     gemm_flops = 2.0 * TOKENS * COLS * ROWS
-    step_bytes = sum(call_bytes(c) for c, _, _ in calls)
+    step_bytes = sum(layer_bytes(c) * nlay for c, _, _, nlay in calls)
     step_flops = gemm_flops * nl
 
     def run_step(events=None):
         for name, ph in phases.items():
             if events is not None:
                 events[name][0].record(stream)
-            for cat, fn, a in ph:
+            for cat, fn, a, _ in ph:
                 st = fn(*a)
                 if st != 0:
                     raise RuntimeError(f"{cat}: {L.tq_status_string(st).decode()}")
@@ -214,17 +217,23 @@ def main():
     ms_per_step = 1e3 * wall / args.steps
     ev_step_ms = float(np.mean([a.elapsed_time(b) for a, b in step_ev]))
 
-    # per category: phase time summed over the timed steps / launches
-    cat_ms, cat_n = {}, {}
-    for s in range(args.steps):
-        for name, ph in phases.items():
-            cat = ph[0][0]
+    # per category: phase time summed over the timed steps / launches; bytes per
+    # launch = the category's algorithmic bytes per step / its launches per step
+    cat_ms, cat_n, cat_layers = {}, {}, {}
+    for name, ph in phases.items():
+        cat = ph[0][0]
+        cat_n[cat] = cat_n.get(cat, 0) + len(ph)
+        cat_layers[cat] = cat_layers.get(cat, 0) + sum(c[3] for c in ph)
+        for s in range(args.steps):
             cat_ms[cat] = cat_ms.get(cat, 0.0) + ev[s][name][0].elapsed_time(ev[s][name][1])
-            cat_n[cat] = cat_n.get(cat, 0) + len(ph)
+
+    def call_bytes(cat):  # average algorithmic bytes per launch of a category
+        return layer_bytes(cat) * cat_layers[cat] / cat_n[cat]
     kernels = {}
     for cat in cat_ms:
-        us = 1e3 * cat_ms[cat] / cat_n[cat]
-        ent = {"launches_per_step": cat_n[cat] // args.steps, "avg_us": round(us, 2)}
+        us = 1e3 * cat_ms[cat] / (cat_n[cat] * args.steps)
+        ent = {"launches_per_step": cat_n[cat], "layers_per_launch": cat_layers[cat] / cat_n[cat],
+               "avg_us": round(us, 2)}
         if cat == "gemm":
             ent["TFLOP/s"] = round(gemm_flops / (us * 1e-6) / 1e12, 1)
             ent["frac_bf16_mfma_peak"] = round(ent["TFLOP/s"] / BF16_MFMA_PEAK_TFLOPS, 4)
@@ -234,12 +243,12 @@ def main():
         kernels[cat] = ent
 
     # mismatch statistics of the last step
-    cnt = CNT.sum(dim=2).cpu().numpy()
-    mism = {"nearest_rate": float(cnt[:, 0, 0].sum() / (nl * n_layer)),
-            "nearest_adjacent_frac": float(cnt[:, 0, 1].sum() / max(cnt[:, 0, 0].sum(), 1))}
+    cnt = CNT.sum(dim=2).cpu().numpy()  # [nearest|guided, layer, (mismatches, adjacent)]
+    mism = {"nearest_rate": float(cnt[0, :, 0].sum() / (nl * n_layer)),
+            "nearest_adjacent_frac": float(cnt[0, :, 1].sum() / max(cnt[0, :, 0].sum(), 1))}
     if nh:
-        mism["hinted_layers_nearest_rate"] = float(cnt[first_hint:, 0, 0].sum() / (nh * n_layer))
-        mism["hinted_layers_guided_rate"] = float(cnt[first_hint:, 1, 0].sum() / (nh * n_layer))
+        mism["hinted_layers_nearest_rate"] = float(cnt[0, first_hint:, 0].sum() / (nh * n_layer))
+        mism["hinted_layers_guided_rate"] = float(cnt[1, first_hint:, 0].sum() / (nh * n_layer))
 
     if args.copy_calibration:
         # one plain device copy of 1 GiB (read 1 GiB, write 1 GiB): the yardstick
@@ -253,14 +262,15 @@ def main():
     # the roofline is reported for the kernel with the largest share of the step
     dom_cat = max(kernels, key=lambda c: kernels[c]["share_of_step"])
     dom = kernels[dom_cat]
-    kname, ksrc = KERNEL_OF[dom_cat]
+    kname = KERNEL_OF[dom_cat][0]
     if dom_cat == "gemm":
         roofline = {"bound": "mfma", "achieved": dom["TFLOP/s"], "peak": BF16_MFMA_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": dom["frac_bf16_mfma_peak"]}
     else:
         roofline = {"bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": dom["frac_hbm_peak"]}
-    roofline.update({"traffic": measured_traffic(dom_cat), "kernel": kname, "category": dom_cat,
+    roofline.update({"traffic": measured_traffic(dom_cat, dom["layers_per_launch"]),
+                     "kernel": kname, "category": dom_cat,
                      "algorithmic_bytes_per_launch": call_bytes(dom_cat),
                      "avg_launch_us": dom["avg_us"], "share_of_step": dom["share_of_step"]})
     if dom_cat == "gemm":
@@ -497,32 +507,40 @@ KERNEL_OF = {
     "gemm": ("tq::grouped_gemm_nvfp4_kernel", "tq_gemm.hip"),
 }
 
-# HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE passes over this
-# benchmark (KiB per dispatch, scaled by what the same counters read for the
-# 1 GiB device copy of --copy-calibration), keyed by the SHA-256 of the kernel's
-# source file when the counters were taken: a changed source reports null.
+# HBM bytes per layer covered, from rocprofv3 FETCH_SIZE and WRITE_SIZE passes
+# over this benchmark (KiB per dispatch scaled by what the same counters read for
+# the 1 GiB device copy of --copy-calibration, divided by the layers the
+# dispatch covers), keyed by the SHA-256 of the kernel's source and the shared
+# device header: a figure is reported only for the code it was measured on.
 TRAFFIC = {
     # FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0: the 1 GiB copy read 524314 KiB fetched and
-    # 1048576 KiB written
-    "amax": {"bytes": 201424606, "fetch_kib": 98324.7, "write_kib": 64.0, "source_sha256": "66319b0f5043f16cbdb70f34304eb9a8013ce2db44bd76cec51d8ef03134c7a9"},
-    "quantize": {"bytes": 258644038, "fetch_kib": 98514.9, "write_kib": 55562.0, "source_sha256": "66319b0f5043f16cbdb70f34304eb9a8013ce2db44bd76cec51d8ef03134c7a9"},
-    "quantize_hint": {"bytes": 270930032, "fetch_kib": 98358.1, "write_kib": 67873.5, "source_sha256": "66319b0f5043f16cbdb70f34304eb9a8013ce2db44bd76cec51d8ef03134c7a9"},
-    "guided": {"bytes": 270629404, "fetch_kib": 104488.0, "write_kib": 55320.8, "source_sha256": "66319b0f5043f16cbdb70f34304eb9a8013ce2db44bd76cec51d8ef03134c7a9"},
-    "mismatch": {"bytes": 100793827, "fetch_kib": 49175.5, "write_kib": 85.3, "source_sha256": "66319b0f5043f16cbdb70f34304eb9a8013ce2db44bd76cec51d8ef03134c7a9"},
-    "sr_transpose": {"bytes": 119785807, "fetch_kib": 27765.2, "write_kib": 61450.7, "source_sha256": "dcf2bfeab6b2b11b602f702b4ef2b00763b153aa944cb93966c0445030938e90"},
-    "gemm": {"bytes": 156472214, "fetch_kib": 43636.6, "write_kib": 65536.0, "source_sha256": "7452e0712dcf97d0d118cc803c6615c432d3d803cc27726d843f7efece17d509"},
+    # 1048576 KiB written.  Ratio to the algorithmic bytes in the comments.
+    "amax": {"bytes_per_layer": 201335411, "fetch_kib": 4718750.7, "write_kib": 96.0, "layers": 48, "sources_sha256": "76be67001684c8d132f92146fed2b0620f79736d976eb3c540840c8d9d37dbd3"},  # 1.000
+    "quantize": {"bytes_per_layer": 258845474, "fetch_kib": 3542447.2, "write_kib": 2015141.8, "layers": 36, "sources_sha256": "76be67001684c8d132f92146fed2b0620f79736d976eb3c540840c8d9d37dbd3"},  # 1.003
+    "quantize_hint": {"bytes_per_layer": 271332715, "fetch_kib": 2359402.2, "write_kib": 1640556.1, "layers": 24, "sources_sha256": "76be67001684c8d132f92146fed2b0620f79736d976eb3c540840c8d9d37dbd3"},  # 1.003
+    "guided": {"bytes_per_layer": 271301931, "fetch_kib": 2506866.1, "write_kib": 1344906.8, "layers": 24, "sources_sha256": "76be67001684c8d132f92146fed2b0620f79736d976eb3c540840c8d9d37dbd3"},  # 1.003
+    "mismatch": {"bytes_per_layer": 100667665, "fetch_kib": 1769500.8, "write_kib": 96.0, "layers": 36, "sources_sha256": "76be67001684c8d132f92146fed2b0620f79736d976eb3c540840c8d9d37dbd3"},  # 1.000
+    "sr_transpose": {"bytes_per_layer": 119554415, "fetch_kib": 663684.7, "write_kib": 1474687.2, "layers": 24, "sources_sha256": "8c03411090b3b9087bf854e0a5cc334e7973875f5f7ea1d5d48789c3f8cf7536"},  # 1.056
+    "gemm": {"bytes_per_layer": 161905869, "fetch_kib": 46287.6, "write_kib": 65536.0, "layers": 1, "sources_sha256": "83e4993ed27dd7fa304f1d13452d58c107e3a962374e8402bd7e7b514b8b13ec"},  # 1.087
 }
 
 
-def measured_traffic(cat):
+def _sources_digest(src):
     import hashlib
+    h = hashlib.sha256()
+    for f in (src, "tq_device.hpp"):
+        with open(os.path.join(ROOT, "fp4_quantization_precision_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(cat, layers_per_launch):
+    """Counter-measured HBM bytes per launch of `cat`, or None if not measured on
+    the current sources."""
     ent = TRAFFIC.get(cat)
-    if ent is None:
+    if ent is None or _sources_digest(KERNEL_OF[cat][1]) != ent["sources_sha256"]:
         return None
-    src = os.path.join(ROOT, "fp4_quantization_precision_amd", "csrc", KERNEL_OF[cat][1])
-    with open(src, "rb") as f:
-        digest = hashlib.sha256(f.read()).hexdigest()
-    return ent["bytes"] if digest == ent["source_sha256"] else None
+    return round(ent["bytes_per_layer"] * layers_per_launch)
 
 
 def cpu_baseline(XR, XT, A, counts, first_hint):
