@@ -257,7 +257,7 @@ void launch_quantize_mxfp8(const void* x, bool bf16, int64_t n, uint8_t* codes, 
     if (blocks == 0)
         return;
     int64_t g = (blocks + 255) / 256;
-    g = g < 4096 ? g : 4096;
+    g = g < (1 << 30) ? g : (1 << 30);  // one block per lane: see the streaming quantizers
     uint4* c4 = reinterpret_cast<uint4*>(codes);
     if (bf16)
         hipLaunchKernelGGL(quantize_mxfp8_kernel<true>, dim3((unsigned)g), dim3(256), 0, s, x, blocks,

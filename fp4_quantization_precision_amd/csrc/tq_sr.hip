@@ -8,7 +8,10 @@
 //
 // One workgroup owns a tile of kTR = 128 input rows x kTC = 256 input columns,
 // so every input row is read as one 128-byte run of codes (plus 16 scale
-// bytes) and every output row of the tile is written as one 64-byte run.
+// bytes) and every output row of the tile is written as one 64-byte run.  The
+// grid is persistent: each workgroup walks a strided list of tiles and loads
+// the next tile's codes and scales into registers while it requantizes the
+// current one.
 //
 // Load phase: a thread takes a pair of input rows and one 32-column chunk,
 // dequantizes them exactly with gfx950's packed FP4 -> f32 conversion
@@ -43,18 +46,14 @@ constexpr int kLdsStride = 68;    // dwords per LDS row: 64 row pairs + 4 pad
 // LDS dword of tile column c, input row pair p
 __device__ __forceinline__ int lds_slot(int c, int p) { return c * kLdsStride + (p ^ (8 * (c >> 5))); }
 
-// Grid spacing above the floor point +-glo, divided by 256, from the exponent
-// bits of glo: 2^-9 below 2 (|glo| in {0, 0.5, 1, 1.5}), then half the power of
-// two of |glo| (2^-8 for 2 and 3, 2^-7 for 4 and 6).
-__device__ __forceinline__ float sr_step(float glo)
-{
-    const int e = (int)(__float_as_uint(glo) & 0x7F800000u) - (9 << 23);
-    return __int_as_float(e > 0x3B000000 ? e : 0x3B000000);
-}
-
 // Stochastic rounding of eight clamped values (|yc| <= 6) with their random
 // bytes k[0..7]: floor codes from the hardware truncation, plus one where the
-// random byte falls below the distance to the floor point.
+// random byte falls below the distance to the floor point.  The grid spacing D
+// above the floor point, divided by 256, is 2^-9 below 2, 2^-8 for 2 and 3 and
+// 2^-7 for 4 and 6; it is decoded from the floor code itself: the magnitude
+// with bit 0 cleared is the code of 0, 1, 2 or 4 (0 for the first two grid
+// points, which is then replaced by the code of 1), and the conversion's
+// power-of-two scale 2^-9 makes that D / 256 exactly.
 __device__ __forceinline__ uint32_t sr_pack8(const float yc[8], const float k[8])
 {
     uint32_t P = 0;
@@ -65,10 +64,18 @@ __device__ __forceinline__ uint32_t sr_pack8(const float yc[8], const float k[8]
     const tq_f32x2 g0 = fp4x2_to_f32<0>(P), g1 = fp4x2_to_f32<1>(P);
     const tq_f32x2 g2 = fp4x2_to_f32<2>(P), g3 = fp4x2_to_f32<3>(P);
     const float g[8] = {g0[0], g0[1], g1[0], g1[1], g2[0], g2[1], g3[0], g3[1]};
+    const uint32_t x = P & 0x66666666u;                                    // m & 6 per nibble
+    const uint32_t nz = (x | (x >> 1)) & 0x22222222u;                      // bit 1: m & 6 != 0
+    const uint32_t Q = x | (nz ^ 0x22222222u);                             // 0 -> code of 1
+    const tq_f32x2 d0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(Q, 0x1p-9f, 0);
+    const tq_f32x2 d1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(Q, 0x1p-9f, 1);
+    const tq_f32x2 d2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(Q, 0x1p-9f, 2);
+    const tq_f32x2 d3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(Q, 0x1p-9f, 3);
+    const float step[8] = {d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], d3[0], d3[1]};
     uint32_t U = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const float t = __builtin_fmaf(k[i], sr_step(g[i]), fabsf(g[i]));  // exact: no rounding occurs
+        const float t = __builtin_fmaf(k[i], step[i], fabsf(g[i]));  // exact: no rounding occurs
         U |= (t < fabsf(yc[i])) ? (1u << (4 * i)) : 0u;
     }
     return clear_negative_zero(P + U);
@@ -88,61 +95,85 @@ __global__ __launch_bounds__(kSThreads, 2) void requant_transpose_sr_kernel(
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int64_t sc_pitch = cols / 16, sct_pitch = rows / 16;
 
-    for (int64_t idx = blockIdx.x; idx < total_tiles; idx += gridDim.x) {
-        // workgroups idx and idx + 8 run on the same XCD: give them the two tiles
-        // that write the two halves of the same 128-byte output runs
+    // tile coordinates of work item idx; workgroups idx and idx + 8 run on the
+    // same XCD: give them the two tiles that write the two halves of the same
+    // 128-byte output runs
+    struct Tile { int64_t b, r0, c0; int rows_valid, cols_valid; bool first; };
+    auto tile_of = [&](int64_t idx) -> Tile {
         const int64_t tile = idx < paired ? (idx & ~(int64_t)15) + 2 * (idx & 7) + ((idx >> 3) & 1) : idx;
         const int64_t b = tile / tiles_per_tensor;
         const int64_t rem = tile - b * tiles_per_tensor;
         const int64_t tc = rem / tiles_r, tr = rem - tc * tiles_r;
         const int64_t r0 = tr * kTR, c0 = tc * kTC;
-        const int rows_valid = (int)(rows - r0 < kTR ? rows - r0 : kTR);  // multiples of 16
-        const int cols_valid = (int)(cols - c0 < kTC ? cols - c0 : kTC);
-        if (tr == 0 && tc == 0 && tid == 0)
-            tensor_scale_t[b] = tensor_scale[b];
-
-        // ---- load + exact dequant: input rows (2p, 2p+1), columns [32h, 32h + 32) ----
-        {
-            const int p = 8 * wave + (lane >> 3), h = lane & 7, cl = 32 * h;
-            int nb = (cols_valid - cl) / 16;
-            nb = nb < 0 ? 0 : (nb > 2 ? 2 : nb);
-            uint32_t w[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-            float d[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
-            if (2 * p < rows_valid && nb > 0) {
+        return {b, r0, c0, (int)(rows - r0 < kTR ? rows - r0 : kTR), (int)(cols - c0 < kTC ? cols - c0 : kTC),
+                tr == 0 && tc == 0};
+    };
+    // load phase operands: input rows (2p, 2p+1), columns [32h, 32h + 32)
+    const int lp = 8 * wave + (lane >> 3), lh = lane & 7, lcl = 32 * lh;
+    struct LRegs { uint32_t w[2][4]; uint32_t s[2]; };
+    auto load = [&](int64_t idx, LRegs& R) {
 #pragma unroll
-                for (int rr = 0; rr < 2; ++rr) {
-                    const int64_t grow = b * rows + r0 + 2 * p + rr;
-                    const uint8_t* src = codes + (grow * cols + c0 + cl) / 2;
-                    if (vec_in && nb == 2) {
-                        const uint4 q = *reinterpret_cast<const uint4*>(src);
-                        w[rr][0] = q.x; w[rr][1] = q.y; w[rr][2] = q.z; w[rr][3] = q.w;
-                    } else {
-                        const uint2 q0 = *reinterpret_cast<const uint2*>(src);
-                        w[rr][0] = q0.x; w[rr][1] = q0.y;
-                        if (nb == 2) {
-                            const uint2 q1 = reinterpret_cast<const uint2*>(src)[1];
-                            w[rr][2] = q1.x; w[rr][3] = q1.y;
-                        }
-                    }
-                    const uint8_t* sp = scales + grow * sc_pitch + (c0 + cl) / 16;
-                    if (vec_scale_in && nb == 2) {
-                        const uint32_t s2 = *reinterpret_cast<const uint16_t*>(sp);
-                        d[rr][0] = e4m3_decode(s2 & 0xFFu);
-                        d[rr][1] = e4m3_decode(s2 >> 8);
-                    } else {
-                        d[rr][0] = e4m3_decode(sp[0]);
-                        if (nb == 2)
-                            d[rr][1] = e4m3_decode(sp[1]);
+        for (int rr = 0; rr < 2; ++rr) {
+            R.w[rr][0] = R.w[rr][1] = R.w[rr][2] = R.w[rr][3] = 0;
+            R.s[rr] = 0;
+        }
+        if (idx >= total_tiles)
+            return;
+        const Tile T = tile_of(idx);
+        int nb = (T.cols_valid - lcl) / 16;
+        nb = nb < 0 ? 0 : (nb > 2 ? 2 : nb);
+        if (2 * lp < T.rows_valid && nb > 0) {
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                const int64_t grow = T.b * rows + T.r0 + 2 * lp + rr;
+                const uint8_t* src = codes + (grow * cols + T.c0 + lcl) / 2;
+                if (vec_in && nb == 2) {
+                    const uint4 q = *reinterpret_cast<const uint4*>(src);
+                    R.w[rr][0] = q.x; R.w[rr][1] = q.y; R.w[rr][2] = q.z; R.w[rr][3] = q.w;
+                } else {
+                    const uint2 q0 = *reinterpret_cast<const uint2*>(src);
+                    R.w[rr][0] = q0.x; R.w[rr][1] = q0.y;
+                    if (nb == 2) {
+                        const uint2 q1 = reinterpret_cast<const uint2*>(src)[1];
+                        R.w[rr][2] = q1.x; R.w[rr][3] = q1.y;
                     }
                 }
+                const uint8_t* sp = scales + grow * sc_pitch + (T.c0 + lcl) / 16;
+                if (vec_scale_in && nb == 2) {
+                    R.s[rr] = *reinterpret_cast<const uint16_t*>(sp);
+                } else {
+                    R.s[rr] = sp[0];
+                    if (nb == 2)
+                        R.s[rr] |= (uint32_t)sp[1] << 8;
+                }
+            }
+        }
+    };
+    LRegs R;
+    load(blockIdx.x, R);
+    for (int64_t idx = blockIdx.x; idx < total_tiles; idx += gridDim.x) {
+        const Tile T = tile_of(idx);
+        const int64_t b = T.b, r0 = T.r0, c0 = T.c0;
+        const int rows_valid = T.rows_valid, cols_valid = T.cols_valid;
+        if (T.first && tid == 0)
+            tensor_scale_t[b] = tensor_scale[b];
+
+        // ---- exact dequant of the prefetched codes into LDS ----
+        {
+            const int p = lp, cl = lcl;
+            float d[2][2];
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                d[rr][0] = e4m3_decode(R.s[rr] & 0xFFu);
+                d[rr][1] = e4m3_decode((R.s[rr] >> 8) & 0xFFu);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float da = d[0][j >> 1], db = d[1][j >> 1];
-                const tq_f32x2 a0 = fp4x2_to_f32<0>(w[0][j]), a1 = fp4x2_to_f32<1>(w[0][j]);
-                const tq_f32x2 a2 = fp4x2_to_f32<2>(w[0][j]), a3 = fp4x2_to_f32<3>(w[0][j]);
-                const tq_f32x2 b0 = fp4x2_to_f32<0>(w[1][j]), b1 = fp4x2_to_f32<1>(w[1][j]);
-                const tq_f32x2 b2 = fp4x2_to_f32<2>(w[1][j]), b3 = fp4x2_to_f32<3>(w[1][j]);
+                const tq_f32x2 a0 = fp4x2_to_f32<0>(R.w[0][j]), a1 = fp4x2_to_f32<1>(R.w[0][j]);
+                const tq_f32x2 a2 = fp4x2_to_f32<2>(R.w[0][j]), a3 = fp4x2_to_f32<3>(R.w[0][j]);
+                const tq_f32x2 b0 = fp4x2_to_f32<0>(R.w[1][j]), b1 = fp4x2_to_f32<1>(R.w[1][j]);
+                const tq_f32x2 b2 = fp4x2_to_f32<2>(R.w[1][j]), b3 = fp4x2_to_f32<3>(R.w[1][j]);
                 const float va[8] = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
                 const float vb[8] = {b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
 #pragma unroll
@@ -150,6 +181,8 @@ __global__ __launch_bounds__(kSThreads, 2) void requant_transpose_sr_kernel(
                     u_s[lds_slot(cl + 8 * j + e, p)] = pack_hi16(va[e] * da, vb[e] * db);
             }
         }
+        // the next tile's codes are in flight during this tile's requantization
+        load(idx + gridDim.x, R);
         __syncthreads();
 
         // ---- requantize: thread -> output row c0 + c, input rows [64 half, 64 half + 64) ----
@@ -241,7 +274,8 @@ void launch_requant_transpose_sr(const uint8_t* codes, const uint8_t* scales,
                                tensor_scale_t, batch);
         return;
     }
-    const int64_t g = total < (1 << 20) ? total : (1 << 20);
+    const int64_t cap = 8192;  // persistent: each workgroup walks tiles, prefetching the next
+    const int64_t g = total < cap ? total : cap;
     const int vec_in = cols % 32 == 0;
     const int vec_scale_in = cols % 32 == 0 && ((uintptr_t)scales & 1u) == 0;
     const int vec_out = rows % 32 == 0;

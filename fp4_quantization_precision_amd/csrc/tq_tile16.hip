@@ -182,7 +182,7 @@ void launch_quantize_tile16(const void* x, bool bf16, int64_t batch, int64_t row
     if (units == 0)
         return;
     int64_t blocks = (units + 3) / 4;
-    blocks = blocks < 8192 ? blocks : 8192;
+    blocks = blocks < (1 << 30) ? blocks : (1 << 30);  // one unit per wave
     uint2* c2 = reinterpret_cast<uint2*>(codes);
     if (bf16)
         hipLaunchKernelGGL(quantize_tile16_kernel<true>, dim3((unsigned)blocks), dim3(kT16Threads), 0,
