@@ -33,6 +33,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "tq_device.hpp"
 #include "tq_kernels.hpp"
 
@@ -81,6 +83,9 @@ __device__ __forceinline__ uint32_t sr_pack8(const float yc[8], const float k[8]
     return clear_negative_zero(P + U);
 }
 
+// WIDE: tile indices need 64 bits; otherwise the per-tile index arithmetic is
+// done in 32 bits (64-bit division is a long instruction sequence).
+template <bool WIDE>
 __global__ __launch_bounds__(kSThreads, 2) void requant_transpose_sr_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const float* __restrict__ tensor_scale, int64_t batch, int64_t rows, int64_t cols,
@@ -99,13 +104,14 @@ __global__ __launch_bounds__(kSThreads, 2) void requant_transpose_sr_kernel(
     // same XCD: give them the two tiles that write the two halves of the same
     // 128-byte output runs
     struct Tile { int64_t b, r0, c0; int rows_valid, cols_valid; bool first; };
+    using I = typename std::conditional<WIDE, uint64_t, uint32_t>::type;
     auto tile_of = [&](int64_t idx) -> Tile {
-        const int64_t tile = idx < paired ? (idx & ~(int64_t)15) + 2 * (idx & 7) + ((idx >> 3) & 1) : idx;
-        const int64_t b = tile / tiles_per_tensor;
-        const int64_t rem = tile - b * tiles_per_tensor;
-        const int64_t tc = rem / tiles_r, tr = rem - tc * tiles_r;
-        const int64_t r0 = tr * kTR, c0 = tc * kTC;
-        return {b, r0, c0, (int)(rows - r0 < kTR ? rows - r0 : kTR), (int)(cols - c0 < kTC ? cols - c0 : kTC),
+        const I tile = (I)(idx < paired ? (idx & ~(int64_t)15) + 2 * (idx & 7) + ((idx >> 3) & 1) : idx);
+        const I b = tile / (I)tiles_per_tensor;
+        const I rem = tile - b * (I)tiles_per_tensor;
+        const I tc = rem / (I)tiles_r, tr = rem - tc * (I)tiles_r;
+        const int64_t r0 = (int64_t)tr * kTR, c0 = (int64_t)tc * kTC;
+        return {(int64_t)b, r0, c0, (int)(rows - r0 < kTR ? rows - r0 : kTR), (int)(cols - c0 < kTC ? cols - c0 : kTC),
                 tr == 0 && tc == 0};
     };
     // load phase operands: input rows (2p, 2p+1), columns [32h, 32h + 32)
@@ -280,10 +286,16 @@ void launch_requant_transpose_sr(const uint8_t* codes, const uint8_t* scales,
     const int vec_scale_in = cols % 32 == 0 && ((uintptr_t)scales & 1u) == 0;
     const int vec_out = rows % 32 == 0;
     const int vec_scale_out = rows % 64 == 0 && ((uintptr_t)scales_t & 3u) == 0;
-    hipLaunchKernelGGL(requant_transpose_sr_kernel, dim3((unsigned)g), dim3(kSThreads), 0, s, codes,
-                       scales, tensor_scale, batch, rows, cols, (uint32_t)seed,
-                       (uint32_t)(seed >> 32), codes_t, scales_t, tensor_scale_t, tiles_r, tiles_c,
-                       vec_in, vec_scale_in, vec_out, vec_scale_out);
+    if (total + g < ((int64_t)1 << 32))
+        hipLaunchKernelGGL(requant_transpose_sr_kernel<false>, dim3((unsigned)g), dim3(kSThreads), 0, s,
+                           codes, scales, tensor_scale, batch, rows, cols, (uint32_t)seed,
+                           (uint32_t)(seed >> 32), codes_t, scales_t, tensor_scale_t, tiles_r, tiles_c,
+                           vec_in, vec_scale_in, vec_out, vec_scale_out);
+    else
+        hipLaunchKernelGGL(requant_transpose_sr_kernel<true>, dim3((unsigned)g), dim3(kSThreads), 0, s,
+                           codes, scales, tensor_scale, batch, rows, cols, (uint32_t)seed,
+                           (uint32_t)(seed >> 32), codes_t, scales_t, tensor_scale_t, tiles_r, tiles_c,
+                           vec_in, vec_scale_in, vec_out, vec_scale_out);
 }
 
 }  // namespace tq
