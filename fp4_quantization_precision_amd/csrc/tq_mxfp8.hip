@@ -17,6 +17,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "tq_device.hpp"
 #include "tq_kernels.hpp"
 
@@ -114,6 +116,10 @@ constexpr int kMTR = 128, kMTC = 256, kMThreads = 512, kMLdsStride = 68;
 
 __device__ __forceinline__ int mlds_slot(int c, int p) { return c * kMLdsStride + (p ^ (8 * (c >> 5))); }
 
+// Persistent: each workgroup walks a strided list of tiles and loads the next
+// tile's codes and scales while it requantizes the current one.  WIDE: tile
+// indices need 64 bits (otherwise the index arithmetic is done in 32 bits).
+template <bool WIDE>
 __global__ __launch_bounds__(kMThreads, 2) void requant_transpose_mxfp8_sr_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const float* __restrict__ tensor_scale, int64_t batch, int64_t rows, int64_t cols,
@@ -127,52 +133,79 @@ __global__ __launch_bounds__(kMThreads, 2) void requant_transpose_mxfp8_sr_kerne
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int64_t sc_pitch = cols / 16, sct_pitch = rows / 32;
 
+    using I = typename std::conditional<WIDE, uint64_t, uint32_t>::type;
+    struct Tile { int64_t b, r0, c0; int rows_valid, cols_valid; bool first; };
+    auto tile_of = [&](int64_t tile_idx) -> Tile {
+        const I tile = (I)tile_idx;
+        const I b = tile / (I)tiles_per_tensor;
+        const I rem = tile - b * (I)tiles_per_tensor;
+        const I tc = rem / (I)tiles_r, tr = rem - tc * (I)tiles_r;
+        const int64_t r0 = (int64_t)tr * kMTR, c0 = (int64_t)tc * kMTC;
+        return {(int64_t)b, r0, c0, (int)(rows - r0 < kMTR ? rows - r0 : kMTR),  // multiples of 32
+                (int)(cols - c0 < kMTC ? cols - c0 : kMTC), tr == 0 && tc == 0};  // multiples of 16
+    };
+    // load phase operands: input rows (2p, 2p+1), columns [32h, 32h + 32)
+    const int lp = 8 * wave + (lane >> 3), lcl = 32 * (lane & 7);
+    struct LRegs { uint32_t w[2][4]; uint32_t s[2]; };
+    auto load = [&](int64_t tile_idx, LRegs& R) {
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) {
+            R.w[rr][0] = R.w[rr][1] = R.w[rr][2] = R.w[rr][3] = 0;
+            R.s[rr] = 0;
+        }
+        if (tile_idx >= total_tiles)
+            return;
+        const Tile T = tile_of(tile_idx);
+        int nb = (T.cols_valid - lcl) / 16;
+        nb = nb < 0 ? 0 : (nb > 2 ? 2 : nb);
+        if (2 * lp < T.rows_valid && nb > 0) {
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                const int64_t grow = T.b * rows + T.r0 + 2 * lp + rr;
+                const uint8_t* src = codes + (grow * cols + T.c0 + lcl) / 2;
+                if (vec_in && nb == 2) {
+                    const uint4 q = *reinterpret_cast<const uint4*>(src);
+                    R.w[rr][0] = q.x; R.w[rr][1] = q.y; R.w[rr][2] = q.z; R.w[rr][3] = q.w;
+                } else {
+                    const uint2 q0 = *reinterpret_cast<const uint2*>(src);
+                    R.w[rr][0] = q0.x; R.w[rr][1] = q0.y;
+                    if (nb == 2) {
+                        const uint2 q1 = reinterpret_cast<const uint2*>(src)[1];
+                        R.w[rr][2] = q1.x; R.w[rr][3] = q1.y;
+                    }
+                }
+                const uint8_t* sp = scales + grow * sc_pitch + (T.c0 + lcl) / 16;
+                R.s[rr] = sp[0];
+                if (nb == 2)
+                    R.s[rr] |= (uint32_t)sp[1] << 8;
+            }
+        }
+    };
+    LRegs R;
+    load(blockIdx.x, R);
     for (int64_t tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
-        const int64_t b = tile / tiles_per_tensor;
-        const int64_t rem = tile - b * tiles_per_tensor;
-        const int64_t tc = rem / tiles_r, tr = rem - tc * tiles_r;
-        const int64_t r0 = tr * kMTR, c0 = tc * kMTC;
-        const int rows_valid = (int)(rows - r0 < kMTR ? rows - r0 : kMTR);  // multiples of 32
-        const int cols_valid = (int)(cols - c0 < kMTC ? cols - c0 : kMTC);  // multiples of 16
-        if (tr == 0 && tc == 0 && tid == 0)
+        const Tile T = tile_of(tile);
+        const int64_t b = T.b, r0 = T.r0, c0 = T.c0;
+        const int rows_valid = T.rows_valid, cols_valid = T.cols_valid;
+        if (T.first && tid == 0)
             tensor_scale_t[b] = tensor_scale[b];
 
-        // ---- load + exact dequant: input rows (2p, 2p+1), columns [32h, 32h + 32) ----
+        // ---- exact dequant of the prefetched codes into LDS ----
         {
-            const int p = 8 * wave + (lane >> 3), h = lane & 7, cl = 32 * h;
-            int nb = (cols_valid - cl) / 16;
-            nb = nb < 0 ? 0 : (nb > 2 ? 2 : nb);
-            uint32_t w[2][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
-            float d[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};
-            if (2 * p < rows_valid && nb > 0) {
+            const int p = lp, cl = lcl;
+            float d[2][2];
 #pragma unroll
-                for (int rr = 0; rr < 2; ++rr) {
-                    const int64_t grow = b * rows + r0 + 2 * p + rr;
-                    const uint8_t* src = codes + (grow * cols + c0 + cl) / 2;
-                    if (vec_in && nb == 2) {
-                        const uint4 q = *reinterpret_cast<const uint4*>(src);
-                        w[rr][0] = q.x; w[rr][1] = q.y; w[rr][2] = q.z; w[rr][3] = q.w;
-                    } else {
-                        const uint2 q0 = *reinterpret_cast<const uint2*>(src);
-                        w[rr][0] = q0.x; w[rr][1] = q0.y;
-                        if (nb == 2) {
-                            const uint2 q1 = reinterpret_cast<const uint2*>(src)[1];
-                            w[rr][2] = q1.x; w[rr][3] = q1.y;
-                        }
-                    }
-                    const uint8_t* sp = scales + grow * sc_pitch + (c0 + cl) / 16;
-                    d[rr][0] = e4m3_decode(sp[0]);
-                    if (nb == 2)
-                        d[rr][1] = e4m3_decode(sp[1]);
-                }
+            for (int rr = 0; rr < 2; ++rr) {
+                d[rr][0] = e4m3_decode(R.s[rr] & 0xFFu);
+                d[rr][1] = e4m3_decode((R.s[rr] >> 8) & 0xFFu);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const float da = d[0][j >> 1], db = d[1][j >> 1];
-                const tq_f32x2 a0 = fp4x2_to_f32<0>(w[0][j]), a1 = fp4x2_to_f32<1>(w[0][j]);
-                const tq_f32x2 a2 = fp4x2_to_f32<2>(w[0][j]), a3 = fp4x2_to_f32<3>(w[0][j]);
-                const tq_f32x2 b0 = fp4x2_to_f32<0>(w[1][j]), b1 = fp4x2_to_f32<1>(w[1][j]);
-                const tq_f32x2 b2 = fp4x2_to_f32<2>(w[1][j]), b3 = fp4x2_to_f32<3>(w[1][j]);
+                const tq_f32x2 a0 = fp4x2_to_f32<0>(R.w[0][j]), a1 = fp4x2_to_f32<1>(R.w[0][j]);
+                const tq_f32x2 a2 = fp4x2_to_f32<2>(R.w[0][j]), a3 = fp4x2_to_f32<3>(R.w[0][j]);
+                const tq_f32x2 b0 = fp4x2_to_f32<0>(R.w[1][j]), b1 = fp4x2_to_f32<1>(R.w[1][j]);
+                const tq_f32x2 b2 = fp4x2_to_f32<2>(R.w[1][j]), b3 = fp4x2_to_f32<3>(R.w[1][j]);
                 const float va[8] = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
                 const float vb[8] = {b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
 #pragma unroll
@@ -180,6 +213,8 @@ __global__ __launch_bounds__(kMThreads, 2) void requant_transpose_mxfp8_sr_kerne
                     u_s[mlds_slot(cl + 8 * j + e, p)] = pack_hi16(va[e] * da, vb[e] * db);
             }
         }
+        // the next tile's codes are in flight during this tile's requantization
+        load(tile + gridDim.x, R);
         __syncthreads();
 
         // ---- requantize: thread -> output row c0 + c, input rows [64 half, 64 half + 64) ----
@@ -280,11 +315,17 @@ void launch_requant_transpose_mxfp8_sr(const uint8_t* codes, const uint8_t* scal
                                tensor_scale_t, batch);
         return;
     }
-    const int64_t g = total < (1 << 20) ? total : (1 << 20);
-    hipLaunchKernelGGL(requant_transpose_mxfp8_sr_kernel, dim3((unsigned)g), dim3(kMThreads), 0, s,
-                       codes, scales, tensor_scale, batch, rows, cols, (uint32_t)seed,
-                       (uint32_t)(seed >> 32), codes_t, scales_t, tensor_scale_t, tiles_r, tiles_c,
-                       (int)(cols % 32 == 0));
+    const int64_t g = total < 8192 ? total : 8192;
+    if (total + g < ((int64_t)1 << 32))
+        hipLaunchKernelGGL(requant_transpose_mxfp8_sr_kernel<false>, dim3((unsigned)g), dim3(kMThreads),
+                           0, s, codes, scales, tensor_scale, batch, rows, cols, (uint32_t)seed,
+                           (uint32_t)(seed >> 32), codes_t, scales_t, tensor_scale_t, tiles_r, tiles_c,
+                           (int)(cols % 32 == 0));
+    else
+        hipLaunchKernelGGL(requant_transpose_mxfp8_sr_kernel<true>, dim3((unsigned)g), dim3(kMThreads),
+                           0, s, codes, scales, tensor_scale, batch, rows, cols, (uint32_t)seed,
+                           (uint32_t)(seed >> 32), codes_t, scales_t, tensor_scale_t, tiles_r, tiles_c,
+                           (int)(cols % 32 == 0));
 }
 
 }  // namespace tq
