@@ -124,30 +124,46 @@ __global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
     uint16_t* __restrict__ out, int n_tiles)
 {
     // Two activation tiles (the one being read, the one being filled), then the
-    // staged scales.  The tile id is passed through the start of the second
-    // activation tile, which is first written after the prologue's barriers.
+    // staged scales; the output tile is staged over the same bytes.
     __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<A_FP4, SLDS>()];
-    int64_t* s_tile = reinterpret_cast<int64_t*>(smem + kATile);
     uint8_t* const Ws = smem + 2 * kATile;            // weight scales [kBN][K/16]
     uint8_t* const As_s = smem + 2 * kATile + kWSTile;  // activation scales [kBM][K/16]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
 
-    // ---- tile id: prefix sum of per-group M-tile counts (wave 0), XCD-aware order ----
-    if (wave == 0) {
-        int64_t carry = 0;
-        int64_t found_e = -1, found_mt = 0;
-        const int64_t b = blockIdx.x;
-        // total tiles first (needed for the XCD split), then locate this tile
+    // ---- tile id, XCD-aware order ----
+    // Every wave computes it (wave-parallel over groups, no barrier): a prefix
+    // sum of per-group M-tile counts.  A lane keeps the offsets of its group of
+    // the first 64, so with at most 64 groups the lookup is one memory round trip.
+    auto uniform64 = [](int64_t v) -> int64_t {
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+        return (int64_t)(((uint64_t)hi << 32) | lo);
+    };
+    auto mtiles = [](int64_t rows) -> int64_t { return rows > 0 ? (rows + kBM - 1) / kBM : 0; };
+    int64_t e, row0, row_end, col0;
+    {
+        int64_t first_lo = 0, first_hi = 0;  // offsets of group `lane`
+        if (lane < num_groups) {
+            first_lo = group_offsets[lane];
+            first_hi = group_offsets[lane + 1];
+        }
+        auto offsets = [&](int g0, int64_t& o0, int64_t& o1) {
+            if (g0 == 0) {
+                o0 = first_lo;
+                o1 = first_hi;
+            } else {
+                const int g = g0 + lane;
+                o0 = g < num_groups ? group_offsets[g] : 0;
+                o1 = g < num_groups ? group_offsets[g + 1] : 0;
+            }
+        };
         int64_t total_m = 0;
         for (int g0 = 0; g0 < num_groups; g0 += 64) {
-            const int g = g0 + lane;
-            int64_t cnt = 0;
-            if (g < num_groups) {
-                const int64_t me = (int64_t)group_offsets[g + 1] - group_offsets[g];
-                cnt = me > 0 ? (me + kBM - 1) / kBM : 0;
-            }
+            int64_t o0, o1;
+            offsets(g0, o0, o1);
+            int64_t cnt = mtiles(o1 - o0);
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1)
                 cnt += __shfl_xor(cnt, off, 64);
@@ -155,16 +171,15 @@ __global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
         }
         const int64_t total = total_m * n_tiles;
         const int64_t per_xcd = (total + 7) / 8;
-        const int64_t L = (b & 7) * per_xcd + (b >> 3);
-        const bool live = (b >> 3) < per_xcd && L < total;
+        const int64_t bx = blockIdx.x;
+        const int64_t L = (bx & 7) * per_xcd + (bx >> 3);
+        const bool live = (bx >> 3) < per_xcd && L < total;
         const int64_t t = live ? L / n_tiles : -1;
+        int64_t found_e = -1, found_r0 = 0, found_r1 = 0, carry = 0;
         for (int g0 = 0; g0 < num_groups && live; g0 += 64) {
-            const int g = g0 + lane;
-            int64_t cnt = 0;
-            if (g < num_groups) {
-                const int64_t me = (int64_t)group_offsets[g + 1] - group_offsets[g];
-                cnt = me > 0 ? (me + kBM - 1) / kBM : 0;
-            }
+            int64_t o0, o1;
+            offsets(g0, o0, o1);
+            const int64_t cnt = mtiles(o1 - o0);
             int64_t incl = cnt;  // inclusive prefix over the 64 lanes
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
@@ -174,8 +189,9 @@ __global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
             }
             const int64_t lo = carry + incl - cnt;
             if (cnt > 0 && t >= lo && t < lo + cnt) {
-                found_e = g;
-                found_mt = t - lo;
+                found_e = g0 + lane;
+                found_r0 = o0 + (t - lo) * kBM;
+                found_r1 = o1;
             }
             carry += __shfl(incl, 63, 64);
         }
@@ -183,32 +199,21 @@ __global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
             const int64_t oe = __shfl_xor(found_e, off, 64);
-            const int64_t om = __shfl_xor(found_mt, off, 64);
+            const int64_t o0 = __shfl_xor(found_r0, off, 64);
+            const int64_t o1 = __shfl_xor(found_r1, off, 64);
             if (oe > found_e) {
                 found_e = oe;
-                found_mt = om;
+                found_r0 = o0;
+                found_r1 = o1;
             }
         }
-        if (lane == 0) {
-            s_tile[0] = live ? found_e : -1;
-            s_tile[1] = found_mt;
-            s_tile[2] = live ? L % n_tiles : 0;
-        }
+        e = uniform64(found_e);
+        row0 = uniform64(found_r0);
+        row_end = uniform64(found_r1);
+        col0 = uniform64(live ? (L % n_tiles) * kBN : 0);
     }
-    __syncthreads();
-    // The tile's coordinates are the same in every lane: keep them in scalar
-    // registers so that every branch on them below is a scalar branch.
-    auto uniform64 = [](int64_t v) -> int64_t {
-        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-        return (int64_t)(((uint64_t)hi << 32) | lo);
-    };
-    const int64_t e = uniform64(s_tile[0]);
     if (e < 0)
         return;
-    const int64_t row0 = uniform64((int64_t)group_offsets[e] + s_tile[1] * kBM);
-    const int64_t row_end = uniform64(group_offsets[e + 1]);
-    const int64_t col0 = uniform64(s_tile[2] * kBN);
     const int kb = (int)(k / 16);  // scale blocks per row
     const int kh = (int)(k / 2);   // code bytes per NVFP4 row
 
@@ -505,28 +510,23 @@ __global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
 
     // ---- epilogue: scale, RNE to bf16, stage the tile in LDS, coalesced stores ----
     const float s_e = A_FP4 ? w_tensor_scale[e] * a_tensor_scale[0] : w_tensor_scale[e];
-    // Lane l holds column l % 32 of rows R (register r, even) and R + 1 (r + 1).
-    // Neighbouring lanes swap one value (DPP quad_perm [1,0,3,2]) so that each
-    // writes one dword of two adjacent columns: the even lane row R at columns
-    // (c, c+1), the odd lane row R + 1 at columns (c-1, c).  The pair is rounded
-    // to bf16 (nearest even) by one packed conversion.
+    // Lane l holds column l % 32 of rows R (register r, even) and R + 1 (r + 1);
+    // one packed conversion rounds the pair to bf16 (nearest even) and its two
+    // halves are written to the two rows of the staged tile.
+    uint16_t* Cs = reinterpret_cast<uint16_t*>(smem);
     uint32_t* Cw = reinterpret_cast<uint32_t*>(smem);
-    const bool odd = lane & 1;
+    const int c_base = (4 * (lane >> 5)) * kCLd + 64 * wave + (lane & 31);
 #pragma unroll
     for (int i = 0; i < kNI; ++i)
 #pragma unroll
         for (int j = 0; j < kNJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
-                const float v0 = acc[i][j][r] * s_e, v1 = acc[i][j][r + 1] * s_e;
-                const float send = odd ? v0 : v1;
-                const float recv = __int_as_float(
-                    __builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
-                const f32x2_t pair = {odd ? recv : v0, odd ? v1 : recv};
+                const f32x2_t pair = {acc[i][j][r] * s_e, acc[i][j][r + 1] * s_e};
                 const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(pair, bf16x2_t));
-                const int row = 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) + (odd ? 1 : 0);
-                const int col = 64 * wave + 32 * j + (lane & 31) - (odd ? 1 : 0);
-                Cw[(row * kCLd + col) >> 1] = w;
+                const int at = c_base + (32 * i + 8 * (r >> 2) + (r & 3)) * kCLd + 32 * j;
+                Cs[at] = (uint16_t)w;
+                Cs[at + kCLd] = (uint16_t)(w >> 16);
             }
     __syncthreads();
     const bool vec_ok = (n % 8) == 0;
