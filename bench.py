@@ -515,13 +515,13 @@ KERNEL_OF = {
 TRAFFIC = {
     # FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0: the 1 GiB copy read 524314 KiB fetched and
     # 1048576 KiB written.  Ratio to the algorithmic bytes in the comments.
-    "amax": {"bytes_per_layer": 201335411, "fetch_kib": 4718750.7, "write_kib": 96.0, "layers": 48, "sources_sha256": "76be67001684c8d132f92146fed2b0620f79736d976eb3c540840c8d9d37dbd3"},  # 1.000
-    "quantize": {"bytes_per_layer": 258845474, "fetch_kib": 3542447.2, "write_kib": 2015141.8, "layers": 36, "sources_sha256": "76be67001684c8d132f92146fed2b0620f79736d976eb3c540840c8d9d37dbd3"},  # 1.003
-    "quantize_hint": {"bytes_per_layer": 271332715, "fetch_kib": 2359402.2, "write_kib": 1640556.1, "layers": 24, "sources_sha256": "76be67001684c8d132f92146fed2b0620f79736d976eb3c540840c8d9d37dbd3"},  # 1.003
-    "guided": {"bytes_per_layer": 271301931, "fetch_kib": 2506866.1, "write_kib": 1344906.8, "layers": 24, "sources_sha256": "76be67001684c8d132f92146fed2b0620f79736d976eb3c540840c8d9d37dbd3"},  # 1.003
-    "mismatch": {"bytes_per_layer": 100667665, "fetch_kib": 1769500.8, "write_kib": 96.0, "layers": 36, "sources_sha256": "76be67001684c8d132f92146fed2b0620f79736d976eb3c540840c8d9d37dbd3"},  # 1.000
-    "sr_transpose": {"bytes_per_layer": 119554415, "fetch_kib": 663684.7, "write_kib": 1474687.2, "layers": 24, "sources_sha256": "8c03411090b3b9087bf854e0a5cc334e7973875f5f7ea1d5d48789c3f8cf7536"},  # 1.056
-    "gemm": {"bytes_per_layer": 161905869, "fetch_kib": 46287.6, "write_kib": 65536.0, "layers": 1, "sources_sha256": "83e4993ed27dd7fa304f1d13452d58c107e3a962374e8402bd7e7b514b8b13ec"},  # 1.087
+    "amax": {"bytes_per_layer": 201335415, "fetch_kib": 4718750.8, "write_kib": 96.0, "layers": 48, "sources_sha256": "0d8f4fa00429875a10b05963f9dd7d2ca3f2a6ebac93643f319102ad91302102"},  # 1.000
+    "quantize": {"bytes_per_layer": 257957939, "fetch_kib": 3539084.0, "write_kib": 1990665.8, "layers": 36, "sources_sha256": "0d8f4fa00429875a10b05963f9dd7d2ca3f2a6ebac93643f319102ad91302102"},  # 1.000
+    "quantize_hint": {"bytes_per_layer": 270541943, "fetch_kib": 2359401.2, "write_kib": 1622024.4, "layers": 24, "sources_sha256": "0d8f4fa00429875a10b05963f9dd7d2ca3f2a6ebac93643f319102ad91302102"},  # 1.000
+    "guided": {"bytes_per_layer": 270540348, "fetch_kib": 2506838.1, "write_kib": 1327113.2, "layers": 24, "sources_sha256": "0d8f4fa00429875a10b05963f9dd7d2ca3f2a6ebac93643f319102ad91302102"},  # 1.000
+    "mismatch": {"bytes_per_layer": 101037759, "fetch_kib": 1769495.5, "write_kib": 13117.7, "layers": 36, "sources_sha256": "0d8f4fa00429875a10b05963f9dd7d2ca3f2a6ebac93643f319102ad91302102"},  # 1.004
+    "sr_transpose": {"bytes_per_layer": 131925355, "fetch_kib": 673323.5, "write_kib": 1745353.5, "layers": 24, "sources_sha256": "9a251d0fee3a08d02369395da522cc150ab579ecef5a17eee7957d9f794d4662"},  # 1.165
+    "gemm": {"bytes_per_layer": 161931059, "fetch_kib": 46299.9, "write_kib": 65536.0, "layers": 1, "sources_sha256": "f3643584a1909714ba00134194c0209223c41707038ab8e4fad26385c4aac293"},  # 1.088
 }
 
 
