@@ -13,8 +13,10 @@
 // lanes of a tile reduce it with cross-lane exchanges; each lane then writes
 // its row's 8 code bytes and lane 0 the tile's scale byte.
 //
-// Transpose: a workgroup moves a 64 x 64 region (4 x 4 tiles) through LDS: 32
-// code bytes per input row in, 32 per output row out, and the 16 tile scales.
+// Transpose: a workgroup moves a 128 x 256 region (8 x 16 tiles): 8 x 8 nibble
+// blocks are transposed in registers and regrouped through LDS, so that input
+// rows are read 128 contiguous bytes at a time and output rows written 64 bytes
+// at a time; the 128 tile scales move one byte each.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -106,59 +108,99 @@ __global__ __launch_bounds__(kT16Threads) void quantize_tile16_kernel(
     }
 }
 
-// Region of 64 x 64 values (4 x 4 tiles) per workgroup iteration.
+// Transpose of an 8 x 8 block of nibbles held as eight dwords (row r in r[r],
+// column k in nibble k): three rounds of swapping the off-diagonal halves of
+// 2 x 2 arrangements of 4 x 4, 2 x 2 and 1 x 1 sub-blocks.
+__device__ __forceinline__ void swap_blocks(uint32_t& a, uint32_t& b, int s, uint32_t lo_mask)
+{
+    const uint32_t na = (a & lo_mask) | ((b << s) & ~lo_mask);
+    const uint32_t nb = ((a >> s) & lo_mask) | (b & ~lo_mask);
+    a = na;
+    b = nb;
+}
+__device__ __forceinline__ void transpose8x8_nibbles(uint32_t r[8])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        swap_blocks(r[i], r[i + 4], 16, 0x0000FFFFu);
+#pragma unroll
+    for (int i = 0; i < 8; i += (i & 1) ? 3 : 1)  // 0, 1, 4, 5
+        swap_blocks(r[i], r[i + 2], 8, 0x00FF00FFu);
+#pragma unroll
+    for (int i = 0; i < 8; i += 2)
+        swap_blocks(r[i], r[i + 1], 4, 0x0F0F0F0Fu);
+}
+
+// Region of kRR x kRC = 128 x 256 values (8 x 16 tiles) per workgroup iteration.
+// Load: a thread takes two 8 x 8 nibble blocks (one dword from each of 8 input
+// rows; the 32 lanes of a half-wave read 128 contiguous bytes of a row) and
+// transposes them in registers; the transposed dwords go to LDS, where an
+// output row (input column) is an LDS row of 16 dwords.  Store: a thread
+// writes one output row's 64 bytes.
+constexpr int kRR = 128, kRC = 256, kTPitch = 17;  // LDS dwords per output row (16 + 1 pad)
+
 __global__ __launch_bounds__(kT16Threads) void transpose_tile16_kernel(
     const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
     const float* __restrict__ tensor_scale, int64_t batch, int64_t rows, int64_t cols,
     uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t,
     float* __restrict__ tensor_scale_t, int64_t regions_r, int64_t regions_c)
 {
-    __shared__ uint2 tile_s[64][4];  // 64 input rows x 32 code bytes
+    __shared__ uint32_t t_s[kRC * kTPitch];
     const int tid = threadIdx.x;
     const int64_t tr = rows / 16, tc = cols / 16;
     const int64_t per_tensor = regions_r * regions_c, total = per_tensor * batch;
+    const bool vec16 = (rows % 32) == 0;
     for (int64_t reg = blockIdx.x; reg < total; reg += gridDim.x) {
         const int64_t b = reg / per_tensor;
         const int64_t rem = reg - b * per_tensor;
         const int64_t rr = rem / regions_c, rc = rem - rr * regions_c;
-        const int64_t r0 = 64 * rr, c0 = 64 * rc;
-        const int rows_valid = (int)(rows - r0 < 64 ? rows - r0 : 64);  // multiples of 16
-        const int cols_valid = (int)(cols - c0 < 64 ? cols - c0 : 64);
+        const int64_t r0 = kRR * rr, c0 = kRC * rc;
+        const int rows_valid = (int)(rows - r0 < kRR ? rows - r0 : kRR);  // multiples of 16
+        const int cols_valid = (int)(cols - c0 < kRC ? cols - c0 : kRC);
         if (rr == 0 && rc == 0 && tid == 0)
             tensor_scale_t[b] = tensor_scale[b];
-        // load: thread -> input row tid / 4, 8-byte chunk tid % 4 (16 columns)
-        {
-            const int r = tid >> 2, q = tid & 3;
-            uint2 w = make_uint2(0, 0);
-            if (r < rows_valid && 16 * q < cols_valid)
-                w = *reinterpret_cast<const uint2*>(codes + ((b * rows + r0 + r) * cols + c0 + 16 * q) / 2);
-            tile_s[r][q] = w;
-        }
-        // tile scales: 16 threads, one tile each
-        if (tid < 16) {
-            const int a = tid >> 2, c = tid & 3;  // tile row / column inside the region
-            if (16 * a < rows_valid && 16 * c < cols_valid) {
-                const int64_t ti = r0 / 16 + a, tj = c0 / 16 + c;
+        // tile scales: one thread per tile of the region
+        if (tid < (kRR / 16) * (kRC / 16)) {
+            const int ta = tid / (kRC / 16), tb = tid % (kRC / 16);  // tile row / column in the region
+            if (16 * ta < rows_valid && 16 * tb < cols_valid) {
+                const int64_t ti = r0 / 16 + ta, tj = c0 / 16 + tb;
                 scales_t[(b * tc + tj) * tr + ti] = scales[(b * tr + ti) * tc + tj];
             }
         }
-        __syncthreads();
-        // transpose: thread -> output row c0 + c (input column), input rows 16 q .. 16 q + 15
-        {
-            const int c = tid >> 2, q = tid & 3;
-            if (c < cols_valid && 16 * q < rows_valid) {
-                const int shift = 4 * (c & 7);
-                const int half = (c & 15) >> 3;  // which dword of the 8-byte chunk
-                const int chunk = c >> 4;
-                uint32_t out[2] = {0, 0};
+        // load and transpose 8 x 8 blocks: block (i, j) = input rows 8 i .., columns 8 j ..
 #pragma unroll
-                for (int m = 0; m < 16; ++m) {
-                    const uint2 w = tile_s[16 * q + m][chunk];
-                    const uint32_t nib = ((half ? w.y : w.x) >> shift) & 15u;
-                    out[m >> 3] |= nib << (4 * (m & 7));
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int blk = tid + kT16Threads * s2;
+            const int i = blk / (kRC / 8), j = blk % (kRC / 8);
+            uint32_t v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            if (8 * i < rows_valid && 8 * j < cols_valid) {
+                const uint32_t* src = reinterpret_cast<const uint32_t*>(
+                    codes + ((b * rows + r0 + 8 * i) * cols + c0 + 8 * j) / 2);
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    v[q] = src[q * (cols / 8)];
+            }
+            transpose8x8_nibbles(v);
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                t_s[(8 * j + q) * kTPitch + i] = v[q];
+        }
+        __syncthreads();
+        // store: thread -> output row c0 + c (input column), input rows r0 .. r0 + rows_valid
+        {
+            const int c = tid;
+            if (c < cols_valid) {
+                uint32_t* dst = reinterpret_cast<uint32_t*>(codes_t + ((b * cols + c0 + c) * rows + r0) / 2);
+                const uint32_t* row = t_s + c * kTPitch;
+                if (vec16 && rows_valid == kRR) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        reinterpret_cast<uint4*>(dst)[q] =
+                            make_uint4(row[4 * q], row[4 * q + 1], row[4 * q + 2], row[4 * q + 3]);
+                } else {
+                    for (int q = 0; q < rows_valid / 16; ++q)
+                        reinterpret_cast<uint2*>(dst)[q] = make_uint2(row[2 * q], row[2 * q + 1]);
                 }
-                *reinterpret_cast<uint2*>(codes_t + ((b * cols + c0 + c) * rows + r0 + 16 * q) / 2) =
-                    make_uint2(out[0], out[1]);
             }
         }
         __syncthreads();
@@ -196,7 +238,7 @@ void launch_transpose_tile16(const uint8_t* codes, const uint8_t* scales, const 
                              int64_t batch, int64_t rows, int64_t cols, uint8_t* codes_t,
                              uint8_t* scales_t, float* tensor_scale_t, hipStream_t s)
 {
-    const int64_t regions_r = (rows + 63) / 64, regions_c = (cols + 63) / 64;
+    const int64_t regions_r = (rows + kRR - 1) / kRR, regions_c = (cols + kRC - 1) / kRC;
     const int64_t total = regions_r * regions_c * batch;
     if (total == 0) {
         if (batch > 0)
