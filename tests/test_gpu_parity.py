@@ -613,6 +613,9 @@ GEMM_EDGES = [
     ([5, 0, 7, 1], 64, 64), ([1], 2, 16), ([130, 3], 66, 80), ([0, 0, 257], 200, 48),
     ([128, 128], 128, 128), ([64] * 5, 256, 2064), ([1, 2, 3, 4, 5, 6, 7], 130, 32),
     ([40, 300], 256, 1040), ([77], 128, 112),
+    # more than 64 groups: the tile lookup walks the group offsets in chunks of 64
+    ([(7 * g) % 23 if g % 5 else 0 for g in range(100)], 64, 96),
+    ([(11 * g) % 37 for g in range(130)], 256, 64),
 ]
 
 
