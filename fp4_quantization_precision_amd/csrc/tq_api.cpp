@@ -161,6 +161,17 @@ TQ_API tq_status tq_requant_transpose_sr(const uint8_t* codes, const uint8_t* sc
     return launch_status();
 }
 
+// The grouped GEMM launches one workgroup per possible 128 x 256 output tile
+// and indexes tiles in 32 bits: m_total fits the int32 group offsets and the
+// tile count stays below 2^31.
+static bool gemm_grid_ok(int64_t m_total, int64_t n, int32_t num_groups)
+{
+    if (m_total > INT32_MAX)
+        return false;
+    const int64_t tiles = ((m_total + 127) / 128 + num_groups) * ((n + 255) / 256);
+    return tiles <= INT32_MAX - 8;
+}
+
 TQ_API tq_status tq_grouped_gemm_nvfp4(const uint16_t* a, const int32_t* group_offsets,
                                        int32_t num_groups, int64_t m_total, int64_t n, int64_t k,
                                        const uint8_t* w_codes, const uint8_t* w_scales,
@@ -170,7 +181,8 @@ TQ_API tq_status tq_grouped_gemm_nvfp4(const uint16_t* a, const int32_t* group_o
         return TQ_ERR_SHAPE;
     int64_t tmp;
     if (!product(m_total, k, 1, &tmp) || !product(m_total, n, 1, &tmp) ||
-        !product(num_groups, n, k, &tmp) || k % 16 != 0 || k > (int64_t(1) << 22) || n % 2 != 0)
+        !product(num_groups, n, k, &tmp) || k % 16 != 0 || k > (int64_t(1) << 22) || n % 2 != 0 ||
+        !gemm_grid_ok(m_total, n, num_groups))
         return TQ_ERR_SHAPE;
     if (!group_offsets)
         return TQ_ERR_NULL;
@@ -299,7 +311,8 @@ TQ_API tq_status tq_grouped_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_s
         return TQ_ERR_SHAPE;
     int64_t tmp;
     if (!product(m_total, k, 1, &tmp) || !product(m_total, n, 1, &tmp) ||
-        !product(num_groups, n, k, &tmp) || k % 16 != 0 || k > (int64_t(1) << 22) || n % 2 != 0)
+        !product(num_groups, n, k, &tmp) || k % 16 != 0 || k > (int64_t(1) << 22) || n % 2 != 0 ||
+        !gemm_grid_ok(m_total, n, num_groups))
         return TQ_ERR_SHAPE;
     if (!group_offsets)
         return TQ_ERR_NULL;

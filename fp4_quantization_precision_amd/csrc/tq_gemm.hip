@@ -55,15 +55,16 @@ constexpr int kBM = 128, kBN = 256, kBK = 64, kGThreads = 256;
 constexpr int kATile = kBM * 128;                 // bf16 activation tile in LDS (128 B rows)
 constexpr int kWSTile = 32768;                    // a tile's weight block scales (kBN rows, K <= 2048)
 constexpr int kASTile = 16384;                    // a tile's activation block scales (kBM rows)
-constexpr int kCLd = kBN + 8;                     // bf16 per LDS row of the staged output
 constexpr int kNI = kBM / 32;                     // MFMA tiles per wave along M
 constexpr int kNJ = 2;                            // MFMA tiles per wave along N (64 columns)
+
+constexpr int kCP = 64 + 4;                       // bf16 per staged output row of one wave
 
 template <bool A_FP4, bool SLDS>
 constexpr int smem_bytes()
 {
     const int ops = 2 * kATile + (SLDS ? kWSTile + (A_FP4 ? kASTile : 0) : 0);
-    const int out = kBM * kCLd * 2;  // staged output tile, reusing the operand space
+    const int out = 4 * kBM * kCP * 2;  // each wave's staged 128 x 64 output block
     return ops > out ? ops : out;
 }
 
@@ -133,86 +134,71 @@ __global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
     const int lane = tid & 63, wave = tid >> 6;
 
     // ---- tile id, XCD-aware order ----
-    // Every wave computes it (wave-parallel over groups, no barrier): a prefix
-    // sum of per-group M-tile counts.  A lane keeps the offsets of its group of
-    // the first 64, so with at most 64 groups the lookup is one memory round trip.
-    auto uniform64 = [](int64_t v) -> int64_t {
-        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-        return (int64_t)(((uint64_t)hi << 32) | lo);
+    // Every wave computes it (no LDS handoff or barrier).  Lane l holds group
+    // g0 + l: its row offsets and M-tile count; an inclusive wave scan of the
+    // counts gives each group's first tile.  The tile's group is the first lane
+    // whose running count passes the tile index (a ballot), and its values are
+    // read from that lane.  With at most 64 groups this is one memory round trip
+    // and one scan.  Tile counts fit 32 bits (the launcher checks).
+    auto mtiles = [](int32_t rows) -> uint32_t { return rows > 0 ? ((uint32_t)rows + kBM - 1) / kBM : 0u; };
+    auto scan = [&](uint32_t v) -> uint32_t {
+        // rows of 16 lanes by row shifts (a lane whose source lies outside its
+        // row adds 0), then the totals of rows 0 and 2 into rows 1 and 3
+        // (broadcast of lane 15 of each row), then that of rows 0-1 into rows
+        // 2-3 (broadcast of lane 31)
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+        v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+        return v;
     };
-    auto mtiles = [](int64_t rows) -> int64_t { return rows > 0 ? (rows + kBM - 1) / kBM : 0; };
-    int64_t e, row0, row_end, col0;
-    {
-        int64_t first_lo = 0, first_hi = 0;  // offsets of group `lane`
-        if (lane < num_groups) {
-            first_lo = group_offsets[lane];
-            first_hi = group_offsets[lane + 1];
-        }
-        auto offsets = [&](int g0, int64_t& o0, int64_t& o1) {
-            if (g0 == 0) {
-                o0 = first_lo;
-                o1 = first_hi;
-            } else {
-                const int g = g0 + lane;
-                o0 = g < num_groups ? group_offsets[g] : 0;
-                o1 = g < num_groups ? group_offsets[g + 1] : 0;
-            }
-        };
-        int64_t total_m = 0;
-        for (int g0 = 0; g0 < num_groups; g0 += 64) {
-            int64_t o0, o1;
-            offsets(g0, o0, o1);
-            int64_t cnt = mtiles(o1 - o0);
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1)
-                cnt += __shfl_xor(cnt, off, 64);
-            total_m += cnt;
-        }
-        const int64_t total = total_m * n_tiles;
-        const int64_t per_xcd = (total + 7) / 8;
-        const int64_t bx = blockIdx.x;
-        const int64_t L = (bx & 7) * per_xcd + (bx >> 3);
-        const bool live = (bx >> 3) < per_xcd && L < total;
-        const int64_t t = live ? L / n_tiles : -1;
-        int64_t found_e = -1, found_r0 = 0, found_r1 = 0, carry = 0;
-        for (int g0 = 0; g0 < num_groups && live; g0 += 64) {
-            int64_t o0, o1;
-            offsets(g0, o0, o1);
-            const int64_t cnt = mtiles(o1 - o0);
-            int64_t incl = cnt;  // inclusive prefix over the 64 lanes
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int64_t v = __shfl_up(incl, off, 64);
-                if (lane >= off)
-                    incl += v;
-            }
-            const int64_t lo = carry + incl - cnt;
-            if (cnt > 0 && t >= lo && t < lo + cnt) {
-                found_e = g0 + lane;
-                found_r0 = o0 + (t - lo) * kBM;
-                found_r1 = o1;
-            }
-            carry += __shfl(incl, 63, 64);
-        }
-        // exactly one lane (or none) found the group
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const int64_t oe = __shfl_xor(found_e, off, 64);
-            const int64_t o0 = __shfl_xor(found_r0, off, 64);
-            const int64_t o1 = __shfl_xor(found_r1, off, 64);
-            if (oe > found_e) {
-                found_e = oe;
-                found_r0 = o0;
-                found_r1 = o1;
-            }
-        }
-        e = uniform64(found_e);
-        row0 = uniform64(found_r0);
-        row_end = uniform64(found_r1);
-        col0 = uniform64(live ? (L % n_tiles) * kBN : 0);
+    int32_t o0 = 0, o1 = 0;  // offsets of group `lane` (first chunk)
+    if (lane < num_groups) {
+        o0 = group_offsets[lane];
+        o1 = group_offsets[lane + 1];
     }
-    if (e < 0)
+    uint32_t cnt = mtiles(o1 - o0);
+    uint32_t incl = scan(cnt);
+    uint32_t total_m = __builtin_amdgcn_readlane(incl, 63);
+    for (int g0 = 64; g0 < num_groups; g0 += 64) {  // more than 64 groups
+        const int g = g0 + lane;
+        uint32_t c = g < num_groups ? mtiles(group_offsets[g + 1] - group_offsets[g]) : 0u;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1)
+            c += __shfl_xor(c, off, 64);
+        total_m += __builtin_amdgcn_readfirstlane(c);
+    }
+    const uint32_t total = total_m * (uint32_t)n_tiles;
+    const uint32_t per_xcd = (total + 7) / 8;
+    const uint32_t bx = blockIdx.x;
+    const uint32_t L = (bx & 7) * per_xcd + (bx >> 3);
+    if ((bx >> 3) >= per_xcd || L >= total)
+        return;
+    const uint32_t t_m = L / (uint32_t)n_tiles;
+    const int64_t col0 = (int64_t)(L - t_m * (uint32_t)n_tiles) * kBN;
+    int64_t e = -1, row0 = 0, row_end = 0;
+    for (uint32_t carry = 0, g0 = 0; g0 < (uint32_t)num_groups; g0 += 64) {
+        if (g0 > 0) {  // next chunk of groups (more than 64 groups)
+            carry += __builtin_amdgcn_readlane(incl, 63);
+            const int g = g0 + lane;
+            o0 = g < num_groups ? group_offsets[g] : 0;
+            o1 = g < num_groups ? group_offsets[g + 1] : 0;
+            cnt = mtiles(o1 - o0);
+            incl = scan(cnt);
+        }
+        const uint64_t hit = __ballot(t_m < carry + incl);
+        if (hit) {
+            const int l = __builtin_ctzll(hit);
+            const uint32_t first = carry + __builtin_amdgcn_readlane(incl - cnt, l);
+            e = g0 + l;
+            row0 = (int64_t)__builtin_amdgcn_readlane(o0, l) + (int64_t)(t_m - first) * kBM;
+            row_end = __builtin_amdgcn_readlane(o1, l);
+            break;
+        }
+    }
+    if (e < 0)  // only with offsets that break the preconditions
         return;
     const int kb = (int)(k / 16);  // scale blocks per row
     const int kh = (int)(k / 2);   // code bytes per NVFP4 row
@@ -481,7 +467,24 @@ __global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
             for (int i = 0; i < NL; ++i)
 #pragma unroll
                 for (int j = 0; j < kNJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][i], bf[c][j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bf[c][j], af[c][i], acc[i][j], 0, 0, 0);
+            if constexpr (SLDS) {
+                // Issue order: the next step's activation fragment reads first,
+                // then each MFMA followed by four VALU operations (the next
+                // step's weight dequantization), so that the reads have a whole
+                // step to land and the dequantization runs between MFMAs.  (The
+                // per-slice scale loads of the other instantiation leave no
+                // registers for this order.)
+                if (kk + 1 < kBK / 16)
+                    __builtin_amdgcn_sched_group_barrier(0x100, NL, 0);  // LDS reads
+#pragma unroll
+                for (int m = 0; m < NL * kNJ; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    if (kk + 1 < kBK / 16)
+                        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         // activations of slice t + 1 into the other tile (zeros past the last
         // slice, into a tile nobody reads again)
@@ -508,43 +511,67 @@ __global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
     else
         run(std::integral_constant<int, 1>{});
 
-    // ---- epilogue: scale, RNE to bf16, stage the tile in LDS, coalesced stores ----
+    // ---- epilogue: scale, RNE to bf16, stage through LDS, coalesced stores ----
+    // The weights are the MFMA's row operand, so lane l of wave w holds
+    // activation row 32 i + l % 32 and, in registers 4 g .. 4 g + 3, the four
+    // consecutive columns 64 w + 32 j + 8 g + 4 h .. + 3: two packed conversions
+    // and one 8-byte LDS write per group.  Each wave stages its own 128 x 64
+    // block (rows of 68 bf16: 16 consecutive rows at one column cover all
+    // banks) and writes it out in 128-byte row segments.  Only the wave itself
+    // reads its block, and LDS operations of one wave complete in order, so no
+    // barrier is needed (the loop's last barrier has retired every read of the
+    // operand tiles this space overlays).
     const float s_e = A_FP4 ? w_tensor_scale[e] * a_tensor_scale[0] : w_tensor_scale[e];
-    // Lane l holds column l % 32 of rows R (register r, even) and R + 1 (r + 1);
-    // one packed conversion rounds the pair to bf16 (nearest even) and its two
-    // halves are written to the two rows of the staged tile.
-    uint16_t* Cs = reinterpret_cast<uint16_t*>(smem);
-    uint32_t* Cw = reinterpret_cast<uint32_t*>(smem);
-    const int c_base = (4 * (lane >> 5)) * kCLd + 64 * wave + (lane & 31);
+    uint16_t* const Cs = reinterpret_cast<uint16_t*>(smem) + wave * (kBM * kCP);
 #pragma unroll
     for (int i = 0; i < kNI; ++i)
 #pragma unroll
         for (int j = 0; j < kNJ; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-                const f32x2_t pair = {acc[i][j][r] * s_e, acc[i][j][r + 1] * s_e};
-                const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(pair, bf16x2_t));
-                const int at = c_base + (32 * i + 8 * (r >> 2) + (r & 3)) * kCLd + 32 * j;
-                Cs[at] = (uint16_t)w;
-                Cs[at + kCLd] = (uint16_t)(w >> 16);
+            for (int g = 0; g < 4; ++g) {
+                const f32x2_t p0 = {acc[i][j][4 * g] * s_e, acc[i][j][4 * g + 1] * s_e};
+                const f32x2_t p1 = {acc[i][j][4 * g + 2] * s_e, acc[i][j][4 * g + 3] * s_e};
+                const uint32_t w0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(p0, bf16x2_t));
+                const uint32_t w1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(p1, bf16x2_t));
+                *reinterpret_cast<uint2*>(Cs + (32 * i + (lane & 31)) * kCP + 32 * j + 8 * g + 4 * h) =
+                    make_uint2(w0, w1);
             }
-    __syncthreads();
-    const bool vec_ok = (n % 8) == 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // lane l writes 16 bytes of rows l / 8 + 8 it at columns 8 (l % 8) of the
+    // wave's 64: all LDS reads first, then the stores
+    const int64_t wc0 = col0 + 64 * wave;
+    const int64_t rows_left = row_end - row0;
+    const int r_l = lane >> 3, c_l = 8 * (lane & 7);
+    uint4 v[kBM / 8];
 #pragma unroll
-    for (int it = 0; it < (kBM * kBN / 8) / kGThreads; ++it) {
-        const int idx = tid + it * kGThreads;
-        const int r = idx / (kBN / 8), c8 = idx % (kBN / 8);
-        const int64_t gr = row0 + r, gc = col0 + 8 * c8;
-        if (gr >= row_end || gc >= n)
-            continue;
-        const uint4 v = *reinterpret_cast<const uint4*>(Cw + ((r * kCLd + 8 * c8) >> 1));
-        uint16_t* dst = out + gr * n + gc;
-        if (vec_ok && gc + 8 <= n) {
-            *reinterpret_cast<uint4*>(dst) = v;
-        } else {
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-            for (int t = 0; t < 8 && gc + t < n; ++t)
-                dst[t] = (uint16_t)(w[t >> 1] >> (16 * (t & 1)));
+    for (int it = 0; it < kBM / 8; ++it) {
+        const uint16_t* s = Cs + (r_l + 8 * it) * kCP + c_l;
+        const uint2 lo = *reinterpret_cast<const uint2*>(s);
+        const uint2 hi = *reinterpret_cast<const uint2*>(s + 4);
+        v[it] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+    uint16_t* const dst0 = out + (row0 + r_l) * n + wc0 + c_l;
+    if ((n % 8) == 0 && wc0 + 64 <= n) {
+#pragma unroll
+        for (int it = 0; it < kBM / 8; ++it)
+            if (r_l + 8 * it < rows_left)
+                *reinterpret_cast<uint4*>(dst0 + 8 * it * n) = v[it];
+    } else {
+        const int64_t gc = wc0 + c_l;
+#pragma unroll
+        for (int it = 0; it < kBM / 8; ++it) {
+            if (r_l + 8 * it >= rows_left || gc >= n)
+                continue;
+            uint16_t* dst = dst0 + 8 * it * n;
+            if ((n % 8) == 0 && gc + 8 <= n) {
+                *reinterpret_cast<uint4*>(dst) = v[it];
+            } else {
+                const uint32_t w[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+                for (int t = 0; t < 8 && gc + t < n; ++t)
+                    dst[t] = (uint16_t)(w[t >> 1] >> (16 * (t & 1)));
+            }
         }
     }
 }

@@ -197,10 +197,12 @@ TQ_API tq_status tq_requant_transpose_sr(const uint8_t* codes, const uint8_t* sc
  *   w_scales       [num_groups][n][k/16] u8.
  *   w_tensor_scale [num_groups] fp32.
  *   out            [m_total][n] bf16 output, 4-byte aligned.
- * Requires k % 16 == 0, 0 <= k <= 2^22, n % 2 == 0, num_groups >= 1 (else
- * TQ_ERR_SHAPE).  Device-side preconditions (not checked): group_offsets
- * nondecreasing with [0] = 0 and [num_groups] = m_total; scale bytes are
- * non-negative E4M3 (0x00..0x7E, as tq_quantize writes them).
+ * Requires k % 16 == 0, 0 <= k <= 2^22, n % 2 == 0, num_groups >= 1,
+ * m_total < 2^31 and (ceil(m_total/128) + num_groups) * ceil(n/256) < 2^31 - 8
+ * (the output tile count; else TQ_ERR_SHAPE).  Device-side preconditions
+ * (not checked): group_offsets nondecreasing with [0] = 0 and
+ * [num_groups] = m_total; scale bytes are non-negative E4M3 (0x00..0x7E,
+ * as tq_quantize writes them).
  * Rows outside every group are left unwritten.
  */
 TQ_API tq_status tq_grouped_gemm_nvfp4(const uint16_t* a, const int32_t* group_offsets,
