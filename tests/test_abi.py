@@ -124,6 +124,8 @@ def test_gemm_validation(L):
     assert call(k=(1 << 22) + 16) == TQ_ERR_SHAPE
     assert call(n=63) == TQ_ERR_SHAPE
     assert call(m=-1) == TQ_ERR_SHAPE
+    assert call(m=2 ** 31) == TQ_ERR_SHAPE                      # beyond int32 group offsets
+    assert call(m=2 ** 31 - 1, n=2 ** 26, k=16) == TQ_ERR_SHAPE  # tile count beyond 32 bits
     assert call(off=NULL) == TQ_ERR_NULL
     assert call(a=NULL) == TQ_ERR_NULL
     assert call(wc=NULL) == TQ_ERR_NULL
@@ -148,6 +150,8 @@ def test_w4a4_gemm_validation(L):
     assert call(k=40) == TQ_ERR_SHAPE
     assert call(k=(1 << 22) + 16) == TQ_ERR_SHAPE
     assert call(n=63) == TQ_ERR_SHAPE
+    assert call(m=2 ** 31) == TQ_ERR_SHAPE
+    assert call(m=2 ** 31 - 1, n=2 ** 26, k=16) == TQ_ERR_SHAPE
     assert call(off=NULL) == TQ_ERR_NULL
     assert call(ac=NULL) == TQ_ERR_NULL
     assert call(as_=NULL) == TQ_ERR_NULL

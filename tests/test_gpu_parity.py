@@ -616,6 +616,9 @@ GEMM_EDGES = [
     # more than 64 groups: the tile lookup walks the group offsets in chunks of 64
     ([(7 * g) % 23 if g % 5 else 0 for g in range(100)], 64, 96),
     ([(11 * g) % 37 for g in range(130)], 256, 64),
+    # exactly 64 and 65 groups (one chunk, and one group into the second); n % 8 == 4
+    ([3 + g % 4 for g in range(64)], 132, 48),
+    ([g % 3 for g in range(65)], 40, 32),
 ]
 
 
