@@ -337,7 +337,8 @@ def measure_extras(L, dev, stream, A, OFF, QG, QN, nl, first_hint):
     * 16x16-tile scaling: quantize and exact transpose of the activations
       workload [32768 x 4096] bf16, and the share of zero codes against block-16;
     * MXFP8 for the backward: nearest quantize of the activations workload and the
-      NVFP4 -> MXFP8 stochastic-rounding transpose of each layer's trainer weights."""
+      NVFP4 -> MXFP8 stochastic-rounding transpose of each layer's trainer weights;
+    * the grouped GEMM at 32 experts, 16384 tokens, K = 2048, N = 768."""
     import ctypes as C
 
     import torch
@@ -381,6 +382,32 @@ def measure_extras(L, dev, stream, A, OFF, QG, QN, nl, first_hint):
         "frac_bf16_mfma_peak": round(flops / us_g / 1e6 / BF16_MFMA_PEAK_TFLOPS, 4),
         "shape": f"{EXPERTS} experts, {TOKENS} tokens, K {COLS}, N {ROWS}"}
     del AQ, OUT
+
+    # ---- grouped GEMM at its own configuration: 32 experts, Zipf(1.1) token
+    # counts summing to 16384, K = 2048, N = 768; four input sets rotate so that
+    # the timed calls do not run from the 256 MB Infinity Cache ----
+    G5, T5, K5, N5 = 32, 16384, 2048, 768
+    sets5 = []
+    for i in range(4):
+        a5, w5, off5 = inputs.grouped_gemm_inputs(G5, T5, K5, N5, device=dev, seed=5 + i)
+        sets5.append((a5, ops.quantize(w5), off5.to(dev)))
+        del w5
+    out5 = torch.empty((T5, N5), dtype=torch.bfloat16, device=dev)
+
+    def gemm_c5():
+        for a5, q5, off5 in sets5:
+            st = L.tq_grouped_gemm_nvfp4(P(a5), P(off5), G5, T5, N5, K5, P(q5.codes), P(q5.scales),
+                                         P(q5.tensor_scale), P(out5), sp)
+            assert st == 0
+
+    us5 = _time_phase(stream, gemm_c5, 5) / len(sets5)
+    flops5 = 2.0 * T5 * K5 * N5
+    out["gemm_32_experts"] = {
+        "kernel": "tq::grouped_gemm_nvfp4_kernel", "avg_us": round(us5, 2),
+        "TFLOP/s": round(flops5 / us5 / 1e6, 1),
+        "frac_bf16_mfma_peak": round(flops5 / us5 / 1e6 / BF16_MFMA_PEAK_TFLOPS, 4),
+        "shape": f"{G5} experts, {T5} tokens, K {K5}, N {N5}, Zipf(1.1) counts"}
+    del sets5, out5
 
     # ---- FP4 KV cache with hints ----
     T, Hh, D = 32768, 8, 128
