@@ -210,7 +210,7 @@ __global__ __launch_bounds__(kMThreads, 2) void requant_transpose_mxfp8_sr_kerne
                 const float vb[8] = {b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    u_s[mlds_slot(cl + 8 * j + e, p)] = pack_hi16(va[e] * da, vb[e] * db);
+                    u_s[mlds_slot(cl + 8 * j + e, p)] = pack_hi16(va[e] * da + 0.0f, vb[e] * db + 0.0f);
             }
         }
         // the next tile's codes are in flight during this tile's requantization
@@ -227,43 +227,73 @@ __global__ __launch_bounds__(kMThreads, 2) void requant_transpose_mxfp8_sr_kerne
                     const int lr = 64 * half + 32 * q;  // first local input row of the block
                     if (lr >= rows_valid)
                         continue;
-                    float u[32];
+                    // the block's 32 staged values as bf16 pairs; a sign bit marks a
+                    // nonzero negative value (zeros were staged as +0)
+                    uint32_t pk[16];
 #pragma unroll
                     for (int part = 0; part < 2; ++part) {
                         const uint4* src = reinterpret_cast<const uint4*>(
                             u_s + c * kMLdsStride + 8 * ((4 * half + 2 * q + part) ^ h));
                         const uint4 v0 = src[0], v1 = src[1];
-                        const uint32_t pk[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) {
-                            u[16 * part + 2 * i] = bf16_lo(pk[i]);
-                            u[16 * part + 2 * i + 1] = bf16_hi(pk[i]);
-                        }
+                        pk[8 * part + 0] = v0.x; pk[8 * part + 1] = v0.y;
+                        pk[8 * part + 2] = v0.z; pk[8 * part + 3] = v0.w;
+                        pk[8 * part + 4] = v1.x; pk[8 * part + 5] = v1.y;
+                        pk[8 * part + 6] = v1.z; pk[8 * part + 7] = v1.w;
                     }
-                    float A = 0.0f;
+                    auto ubits = [&](int e) -> uint32_t {  // binary32 bits of element e
+                        return (e & 1) ? (pk[e >> 1] & 0xFFFF0000u) : (pk[e >> 1] << 16);
+                    };
+                    uint32_t Ab = 0;  // |u| bits: integer order = value order
 #pragma unroll
-                    for (int i = 0; i < 32; ++i)
-                        A = fmaxf(A, fabsf(u[i]));
+                    for (int e = 0; e < 32; ++e)
+                        Ab = max(Ab, ubits(e) & 0x7FFFFFFFu);
                     const int64_t obase = (b * cols + oc) * rows + r0 + lr;  // output linear index
                     uint32_t wout[8] = {0, 0, 0, 0, 0, 0, 0, 0};
                     uint32_t sb = 0;
-                    if (A != 0.0f) {
-                        const int se = mx_shared_exp(A);
+                    if (Ab != 0) {
+                        const int se = mx_shared_exp(__uint_as_float(Ab));
                         sb = (uint32_t)(se + 127);
+                        // Integer path, valid when every nonzero y = u * 2^-se is at
+                        // least 2^-6 (E4M3 normal range).  With X = bits(|y|) -
+                        // (120 << 23) = bits(|u|) - ((se + 120) << 23), the floor code
+                        // is X >> 20 (exponent - 120, three mantissa bits) and the
+                        // spacing above it is 2^20 units of X, so the step up
+                        // (k < 256 * frac) is "X mod 2^20 > k * 2^12": one carry,
+                        // (X + 2^20 - 1 - k * 2^12) >> 20.  Codes past 0x7E clamp
+                        // (|y| >= 448 gives 448), and zeros give X = 0 and code 0.
+                        const int kexp = se + 120;
+                        uint32_t nzmin = 0xFFFFFFFFu;  // smallest nonzero |u| bits, less one
+#pragma unroll
+                        for (int e = 0; e < 32; ++e)
+                            nzmin = min(nzmin, (ubits(e) & 0x7FFFFFFFu) - 1u);
+                        const bool fast = kexp > 0 && nzmin >= ((uint32_t)(kexp + 1) << 23) - 1u;
+                        const uint32_t K = (uint32_t)kexp << 23;
 #pragma unroll
                         for (int part = 0; part < 2; ++part) {
                             const uint64_t beta = (uint64_t)(obase / 16) + part;
                             const u32x4 rnd = philox4x32_10((uint32_t)beta, (uint32_t)(beta >> 32), 0u,
                                                             0u, seed_lo, seed_hi);
                             const uint32_t rw[4] = {rnd.x, rnd.y, rnd.z, rnd.w};
+                            if (fast) {
 #pragma unroll
-                            for (int i = 0; i < 16; ++i) {
-                                const float y = __builtin_ldexpf(u[16 * part + i], -se);
-                                const float k = (float)((rw[i >> 2] >> (8 * (i & 3))) & 0xFFu);
-                                const uint32_t m = e4m3_sr_code(fabsf(y), k);
-                                const uint32_t code = (y < 0.0f && m != 0u) ? (0x80u | m) : m;
-                                const int e = 16 * part + i;
-                                wout[e >> 2] |= code << (8 * (e & 3));
+                                for (int i = 0; i < 16; ++i) {
+                                    const int e = 16 * part + i;
+                                    const uint32_t bits = ubits(e);
+                                    const int32_t X = max((int32_t)((bits & 0x7FFFFFFFu) - K), 0);
+                                    const uint32_t k12 = ((rw[i >> 2] >> (8 * (i & 3))) & 0xFFu) << 12;
+                                    const uint32_t m = min(((uint32_t)X + 0xFFFFFu - k12) >> 20, 0x7Eu);
+                                    wout[e >> 2] |= (m | ((bits >> 24) & 0x80u)) << (8 * (e & 3));
+                                }
+                            } else {
+#pragma unroll
+                                for (int i = 0; i < 16; ++i) {
+                                    const int e = 16 * part + i;
+                                    const float y = __builtin_ldexpf(__uint_as_float(ubits(e)), -se);
+                                    const float k = (float)((rw[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+                                    const uint32_t m = e4m3_sr_code(fabsf(y), k);
+                                    const uint32_t code = (y < 0.0f && m != 0u) ? (0x80u | m) : m;
+                                    wout[e >> 2] |= code << (8 * (e & 3));
+                                }
                             }
                         }
                     }
