@@ -548,7 +548,7 @@ TRAFFIC = {
     "guided": {"bytes_per_layer": 270540348, "fetch_kib": 2506838.1, "write_kib": 1327113.2, "layers": 24, "sources_sha256": "0d8f4fa00429875a10b05963f9dd7d2ca3f2a6ebac93643f319102ad91302102"},  # 1.000
     "mismatch": {"bytes_per_layer": 101037759, "fetch_kib": 1769495.5, "write_kib": 13117.7, "layers": 36, "sources_sha256": "0d8f4fa00429875a10b05963f9dd7d2ca3f2a6ebac93643f319102ad91302102"},  # 1.004
     "sr_transpose": {"bytes_per_layer": 131925355, "fetch_kib": 673323.5, "write_kib": 1745353.5, "layers": 24, "sources_sha256": "9a251d0fee3a08d02369395da522cc150ab579ecef5a17eee7957d9f794d4662"},  # 1.165
-    "gemm": {"bytes_per_layer": 159268532, "fetch_kib": 45002.0, "write_kib": 65536.0, "layers": 1, "sources_sha256": "6cac751a420bfd153dd3963d1993cc1827d438b284fbad10d39d9433a914059e"},  # 1.070
+    "gemm": {"bytes_per_layer": 159268532, "fetch_kib": 45002.0, "write_kib": 65536.0, "layers": 1, "sources_sha256": "56b93a30f9f2d805d2bcc31c6c0b690b08abbabcc2632fc05ae18bd2c1d89dd8"},  # 1.070
 }
 
 

@@ -10,7 +10,10 @@
 //
 // Work decomposition.  One workgroup (4 waves) computes a kBM x kBN = 128 x 256
 // output tile of one group (expert); wave w owns all 128 rows and columns
-// 64 w .. 64 w + 63 as 4 x 2 MFMA 32x32x16 tiles.  Only the activations go
+// 64 w .. 64 w + 63 as 4 x 2 MFMA 32x32x16 tiles, with the weights as the
+// MFMA's row operand and the activations as its column operand (so a lane's
+// accumulators hold one output row and runs of four consecutive columns, which
+// the epilogue stages with 8-byte LDS writes).  Only the activations go
 // through LDS (each wave reads all of them: 0.5 KiB of LDS per MFMA); the
 // weight codes go straight from memory to the registers of the lanes that feed
 // them to the MFMA and are dequantized there, so no weight value is written to
@@ -19,7 +22,8 @@
 // kk-th MFMA, which makes a lane's weights for one column 32 consecutive codes
 // (one 16-byte load) and its activations chunk 4 h + kk of the LDS row.
 // The tile list is derived on the device from the group offsets (a wave-wide
-// prefix sum of per-group tile counts), so no host synchronisation is needed.
+// prefix scan of per-group tile counts, then a ballot for the tile's group), so
+// no host synchronisation is needed.
 // Consecutive workgroup ids are dealt round-robin to the 8 XCDs; the id -> tile
 // map undoes that, so each XCD walks a contiguous run of tiles in (M-tile,
 // N-tile) order and the N-tiles of one M-tile share their activation rows
@@ -36,7 +40,8 @@
 // activations are written to the other of two LDS tiles at the end of the
 // slice, so one barrier per slice suffices.  The fragments of MFMA step kk + 1
 // (weights dequantized, activations read) are produced while the MFMAs of step
-// kk run.  All operand loads are buffer loads against per-workgroup resources:
+// kk run, in a fixed issue order: the fragment reads first, then one MFMA per
+// four dequantization VALU instructions.  All operand loads are buffer loads against per-workgroup resources:
 // the per-thread byte offsets are fixed for the whole K loop and the slice
 // position is a scalar offset, and rows past the end of A or W read as zeros in
 // hardware (such rows only feed output rows or columns that are never stored).
