@@ -217,12 +217,27 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     uint8_t* __restrict__ scales, float* __restrict__ tensor_scale,
     uint16_t* __restrict__ hints, int64_t total_blocks)
 {
-    for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
+    // Consecutive workgroups are dealt to the 8 XCDs in turn.  For the nearest
+    // modes, when the grid has a multiple of 8 workgroups, they are renumbered
+    // so that each XCD streams a contiguous eighth of the launch (3.5% faster on
+    // the MoE-weights workload; the guided mode, which also reads the hints,
+    // ran 4.5% slower with it and keeps the plain order).
+    uint32_t bx = blockIdx.x, by = blockIdx.y;
+    if constexpr (MODE != MODE_GUIDED) {
+        const uint64_t G = (uint64_t)gridDim.x * gridDim.y;
+        if ((G & 7) == 0) {
+            const uint64_t L = (uint64_t)by * gridDim.x + bx;
+            const uint64_t R = (L & 7) * (G >> 3) + (L >> 3);
+            by = (uint32_t)(R / gridDim.x);
+            bx = (uint32_t)(R - (uint64_t)by * gridDim.x);
+        }
+    }
+    for (int64_t b = by; b < batch; b += gridDim.y) {
         const float A_T = tensor_amax[b];
         const float s_t = (A_T == 0.0f) ? 0.0f : A_T / 2688.0f;
-        if (blockIdx.x == 0 && threadIdx.x == 0)
+        if (bx == 0 && threadIdx.x == 0)
             tensor_scale[b] = s_t;
-        for (int64_t j = (int64_t)blockIdx.x * kThreads + threadIdx.x; j < blocks_per_tensor;
+        for (int64_t j = (int64_t)bx * kThreads + threadIdx.x; j < blocks_per_tensor;
              j += (int64_t)gridDim.x * kThreads) {
             const int64_t blk = b * blocks_per_tensor + j;
             float v[16];

@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "tq_device.hpp"
 #include "tq_kernels.hpp"
 
@@ -52,40 +54,58 @@ __device__ __forceinline__ void load_row16(const void* __restrict__ x, int64_t e
     }
 }
 
-template <bool BF16>
+// Maximum over the 16 lanes of a DPP row (one tile): quad exchanges (lane ^ 1,
+// lane ^ 2), then the half-row and row mirrors, which pair the quads.
+__device__ __forceinline__ uint32_t row16_max(uint32_t v)
+{
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+    return v;
+}
+
+// WIDE: unit indices need 64 bits; otherwise they are split with 32-bit
+// arithmetic.  The unit index is wave-uniform, so the split runs on the scalar
+// unit.
+template <bool BF16, bool WIDE>
 __global__ __launch_bounds__(kT16Threads) void quantize_tile16_kernel(
     const void* __restrict__ x, int64_t batch, int64_t rows, int64_t cols,
     const float* __restrict__ tensor_amax, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
     float* __restrict__ tensor_scale, int64_t units)
 {
+    typedef typename std::conditional<WIDE, uint64_t, uint32_t>::type I;
     const int lane = threadIdx.x & 63, t = lane >> 4, j = lane & 15;
-    const int64_t tr = rows / 16, tc = cols / 16, groups = (tc + 3) / 4;
-    const int64_t waves_total = (int64_t)gridDim.x * (kT16Threads / 64);
-    const int64_t wave_id = (int64_t)blockIdx.x * (kT16Threads / 64) + (threadIdx.x >> 6);
-    for (int64_t u = wave_id; u < units; u += waves_total) {
+    const I tr = (I)(rows / 16), tc = (I)(cols / 16), groups = (tc + 3) / 4;
+    const I per_tensor = tr * groups;
+    const I waves_total = (I)gridDim.x * (kT16Threads / 64);
+    // Consecutive workgroups are dealt to the 8 XCDs in turn; the remap gives
+    // each XCD a contiguous run of units (6% over the plain order).
+    const I per_xcd = ((I)gridDim.x + 7) / 8;
+    const I bx = (I)blockIdx.x;
+    const I blk = (bx & 7) * per_xcd + (bx >> 3);
+    const I wave_id = blk * (kT16Threads / 64) + (I)__builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (I u = wave_id; u < (I)units; u += waves_total) {
         // unit = (tensor b, tile row ti, group of four tile columns g)
-        const int64_t b = u / (tr * groups);
-        const int64_t rem = u - b * tr * groups;
-        const int64_t ti = rem / groups, g = rem - ti * groups;
-        const int64_t tj = 4 * g + t;
+        const I b = u / per_tensor;
+        const I rem = u - b * per_tensor;
+        const I ti = rem / groups, g = rem - ti * groups;
+        const I tj = 4 * g + (I)t;
         const bool live = tj < tc;  // the last group of a row may hold fewer tiles
         const float A_T = tensor_amax[b];
         const float s_t = (A_T == 0.0f) ? 0.0f : A_T / 2688.0f;
         if (ti == 0 && g == 0 && lane == 0)
             tensor_scale[b] = s_t;
-        const int64_t elem = (b * rows + 16 * ti + j) * cols + 16 * tj;
+        const int64_t elem = ((int64_t)b * rows + 16 * (int64_t)ti + j) * cols + 16 * (int64_t)tj;
         float v[16];
-        float A = 0.0f;
+        uint32_t Ab = 0;  // |x| bits: integer order = value order
         if (live) {
             load_row16<BF16>(x, elem, v);
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                A = fmaxf(A, fabsf(v[i]));
+                Ab = max(Ab, __float_as_uint(v[i]) & 0x7FFFFFFFu);
         }
-        // tile maximum over the 16 lanes of the tile
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1)
-            A = fmaxf(A, __shfl_xor(A, off, 64));
+        const float A = __uint_as_float(row16_max(Ab));  // tile maximum
         if (!live)
             continue;
         uint32_t e = 0;
@@ -104,7 +124,7 @@ __global__ __launch_bounds__(kT16Threads) void quantize_tile16_kernel(
         }
         codes[elem / 16] = make_uint2(lo, hi);
         if (j == 0)
-            scales[(b * tr + ti) * tc + tj] = (uint8_t)e;
+            scales[((int64_t)b * tr + ti) * tc + tj] = (uint8_t)e;
     }
 }
 
@@ -225,13 +245,25 @@ void launch_quantize_tile16(const void* x, bool bf16, int64_t batch, int64_t row
         return;
     int64_t blocks = (units + 3) / 4;
     blocks = blocks < (1 << 30) ? blocks : (1 << 30);  // one unit per wave
+    blocks = (blocks + 7) / 8 * 8;  // the XCD remap is a permutation only of a multiple of 8
     uint2* c2 = reinterpret_cast<uint2*>(codes);
-    if (bf16)
-        hipLaunchKernelGGL(quantize_tile16_kernel<true>, dim3((unsigned)blocks), dim3(kT16Threads), 0,
-                           s, x, batch, rows, cols, tensor_amax, c2, scales, tensor_scale, units);
-    else
-        hipLaunchKernelGGL(quantize_tile16_kernel<false>, dim3((unsigned)blocks), dim3(kT16Threads),
-                           0, s, x, batch, rows, cols, tensor_amax, c2, scales, tensor_scale, units);
+    // 32-bit unit arithmetic when every index it forms fits
+    const bool wide = units + 4 * blocks >= (int64_t(1) << 32) || batch * (rows / 16) * (cols / 16) >= (int64_t(1) << 32);
+#define TQ_T16_LAUNCH(B, W)                                                                        \
+    hipLaunchKernelGGL((quantize_tile16_kernel<B, W>), dim3((unsigned)blocks), dim3(kT16Threads), 0, s, \
+                       x, batch, rows, cols, tensor_amax, c2, scales, tensor_scale, units)
+    if (bf16) {
+        if (wide)
+            TQ_T16_LAUNCH(true, true);
+        else
+            TQ_T16_LAUNCH(true, false);
+    } else {
+        if (wide)
+            TQ_T16_LAUNCH(false, true);
+        else
+            TQ_T16_LAUNCH(false, false);
+    }
+#undef TQ_T16_LAUNCH
 }
 
 void launch_transpose_tile16(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,

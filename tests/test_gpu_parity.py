@@ -439,7 +439,8 @@ def test_mxfp8_sr_transpose_full_size():
 # ----------------------------------------------------------------------------------
 
 TILE16_SHAPES = [(1, 16, 16, "f32"), (1, 48, 80, "bf16"), (3, 272, 96, "bf16"), (2, 16, 1040, "f32"),
-                 (1, 64, 64, "bf16"), (2, 528, 144, "bf16"), (1, 1024, 1024, "f32")]
+                 (1, 64, 64, "bf16"), (2, 528, 144, "bf16"), (1, 1024, 1024, "f32"),
+                 (1, 592, 832, "bf16")]  # 481 wave units: a grid that is not a multiple of 8 workgroups
 
 
 @pytest.mark.parametrize("shape", TILE16_SHAPES)
