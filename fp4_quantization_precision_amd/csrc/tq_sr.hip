@@ -28,8 +28,9 @@
 // value comes from v_cvt_scalef32_sr_pk_fp4_f32 with a zero seed (which
 // truncates to the grid toward zero, sign kept), its value from the packed
 // decode; the step up is taken iff G[lo] + k * D / 256 < |y| with D the grid
-// spacing above G[lo] (all terms exact), and values are first clamped to
-// [-6, 6] so that saturation needs no separate case.
+// spacing above G[lo] (all terms exact).  Values above 6 in magnitude (the
+// E4M3 block scale may round down) truncate to the top code, whose step up is
+// masked off, so saturation needs no per-value clamp.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -48,9 +49,10 @@ constexpr int kLdsStride = 68;    // dwords per LDS row: 64 row pairs + 4 pad
 // LDS dword of tile column c, input row pair p
 __device__ __forceinline__ int lds_slot(int c, int p) { return c * kLdsStride + (p ^ (8 * (c >> 5))); }
 
-// Stochastic rounding of eight clamped values (|yc| <= 6) with their random
-// bytes k[0..7]: floor codes from the hardware truncation, plus one where the
-// random byte falls below the distance to the floor point.  The grid spacing D
+// Stochastic rounding of eight values with their random bytes k[0..7]: floor
+// codes from the hardware truncation (saturating at 6), plus one where the
+// random byte falls below the distance to the floor point, except from the top
+// code.  The grid spacing D
 // above the floor point, divided by 256, is 2^-9 below 2, 2^-8 for 2 and 3 and
 // 2^-7 for 4 and 6; it is decoded from the floor code itself: the magnitude
 // with bit 0 cleared is the code of 0, 1, 2 or 4 (0 for the first two grid
@@ -74,12 +76,21 @@ __device__ __forceinline__ uint32_t sr_pack8(const float yc[8], const float k[8]
     const tq_f32x2 d2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(Q, 0x1p-9f, 2);
     const tq_f32x2 d3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(Q, 0x1p-9f, 3);
     const float step[8] = {d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], d3[0], d3[1]};
-    uint32_t U = 0;
+    // Step up iff t = |g| + k * step < |y|, i.e. iff t - |y| is negative: the
+    // sum t is exact and a rounded difference keeps the sign of the exact one
+    // (an exact zero is +0, not a step).  Each difference's top nibble is
+    // shifted into an accumulator, last value first, so that value i's sign bit
+    // lands on bit 3 of nibble i.
+    uint32_t acc = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 7; i >= 0; --i) {
         const float t = __builtin_fmaf(k[i], step[i], fabsf(g[i]));  // exact: no rounding occurs
-        U |= (t < fabsf(yc[i])) ? (1u << (4 * i)) : 0u;
+        acc = __builtin_amdgcn_alignbit(acc, __float_as_uint(t - fabsf(yc[i])), 28);
     }
+    uint32_t U = (acc >> 3) & 0x11111111u;
+    // |y| may exceed 6 (the block scale is rounded to E4M3); its floor is then
+    // the top code 7, which never steps up: clear the step of magnitude-7 nibbles
+    U &= ~(P & (P >> 1) & (P >> 2));
     return clear_negative_zero(P + U);
 }
 
@@ -230,7 +241,7 @@ __global__ __launch_bounds__(kSThreads, 2) void requant_transpose_sr_kernel(
                     float yc[16], k[16];
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        yc[i] = __builtin_amdgcn_fmed3f(u[i] * rcp, -6.0f, 6.0f);
+                        yc[i] = u[i] * rcp;
                         k[i] = (float)((rw[i >> 2] >> (8 * (i & 3))) & 0xFFu);
                     }
                     if (dec != 0.0f) {
