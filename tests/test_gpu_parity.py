@@ -533,6 +533,31 @@ def test_transpose_sr_shapes(shape):
         assert np.array_equal(npu8(t.tensor_scale), o["tensor_scale"])
 
 
+def test_transpose_sr_on_grid_exact():
+    """Every requantized value on the grid (one scale for the whole tensor and a 6
+    in every new block): for every seed the transpose reproduces the input codes,
+    with -0 written as +0 -- the step-up test must treat t == |y| as no step."""
+    B, R, Cc = 1, 64, 96
+    rng = np.random.default_rng(17)
+    codes4 = rng.integers(0, 16, size=(R, Cc), dtype=np.uint8)
+    codes4[::16, :] = np.where(rng.random(Cc) < 0.5, 7, 15).astype(np.uint8)  # +-6 in each new block
+    packed = (codes4[:, 0::2] | (codes4[:, 1::2] << 4)).astype(np.uint8).reshape(-1)
+    c = torch.from_numpy(packed)
+    s = torch.full((R * Cc // 16,), 0x38, dtype=torch.uint8)  # every block scale 1.0
+    ts = torch.ones(1, dtype=torch.float32)
+    q = ops.NVFP4(c.to(DEV), s.to(DEV), ts.to(DEV), torch.zeros(B, device=DEV))
+    want = codes4.T.copy()
+    want[want == 8] = 0
+    want_packed = (want[:, 0::2] | (want[:, 1::2] << 4)).astype(np.uint8).reshape(-1)
+    for seed in range(4):
+        t = ops.requant_transpose_sr(q, B, R, Cc, seed=seed)
+        torch.cuda.synchronize()
+        o = oracle.requant_transpose_sr(c, s, ts, B, R, Cc, seed)
+        assert np.array_equal(npu8(t.codes), o["codes"]), f"seed {seed}"
+        assert np.array_equal(npu8(t.codes), want_packed), f"seed {seed}"
+        assert np.all(npu8(t.scales) == 0x38)
+
+
 def test_transpose_sr_64_seeds_unbiased():
     """All 64 seeds on a 1024x1024 tensor nearest-quantized from N(0,1): bit-exact
     against the oracle, and the mean over seeds of the requantized values tracks
