@@ -72,14 +72,14 @@ def lib():
         L.tqo_sr_byte.restype = i32
         L.tqo_sr_index.argtypes = [C.c_float, i32]
         L.tqo_sr_index.restype = i32
-        L.tqo_requant_transpose_sr.argtypes = [p, p, p, i64, i64, i64, C.c_uint64, p, p, p]
+        L.tqo_requant_transpose_sr.argtypes = [p, p, p, i64, i64, i64, C.c_uint64, p, p, p, i64]
         L.tqo_grouped_gemm.argtypes = [p, p, C.c_int32, i64, i64, p, p, p, p, i64, p, p]
         L.tqo_e8m0_value.argtypes = [C.c_uint8]
         L.tqo_e8m0_value.restype = C.c_double
         L.tqo_e4m3_sr.argtypes = [C.c_float, i32]
         L.tqo_e4m3_sr.restype = i32
         L.tqo_quantize_mxfp8.argtypes = [p, i32, i64, i64, i64, p, p]
-        L.tqo_requant_transpose_mxfp8_sr.argtypes = [p, p, p, i64, i64, i64, C.c_uint64, p, p, p]
+        L.tqo_requant_transpose_mxfp8_sr.argtypes = [p, p, p, i64, i64, i64, C.c_uint64, p, p, p, i64]
         L.tqo_quantize_tile16.argtypes = [p, i32, i64, i64, i64, i32, p, p, p, p]
         L.tqo_transpose_tile16.argtypes = [p, p, p, i64, i64, i64, p, p, p]
         L.tqo_grouped_gemm_w4a4.argtypes = [p, p, p, p, C.c_int32, i64, i64, p, p, p, p, i64, p, p]
@@ -232,14 +232,17 @@ def sr_byte(seed: int, i: int) -> int:
     return int(lib().tqo_sr_byte(int(seed), int(i)))
 
 
-def requant_transpose_sr(codes, scales, tensor_scale, batch: int, rows: int, cols: int, seed: int):
+def requant_transpose_sr(codes, scales, tensor_scale, batch: int, rows: int, cols: int, seed: int,
+                         first: int = 0):
+    """first: index of tensor 0 of this call within a larger batch (random-byte indices
+    are those of the whole batch, outputs start at 0)."""
     c, s = _np(codes, np.uint8), _np(scales, np.uint8)
     t = _np(tensor_scale, np.float32)
     assert rows % 16 == 0 and cols % 16 == 0
     n = batch * rows * cols
     ct, st, tt = np.zeros(n // 2, np.uint8), np.zeros(n // 16, np.uint8), np.zeros(batch, np.float32)
     lib().tqo_requant_transpose_sr(_ptr(c), _ptr(s), _ptr(t), batch, rows, cols, int(seed),
-                                   _ptr(ct), _ptr(st), _ptr(tt))
+                                   _ptr(ct), _ptr(st), _ptr(tt), int(first))
     return dict(codes=ct, scales=st, tensor_scale=tt)
 
 
@@ -278,8 +281,9 @@ def quantize_mxfp8(x, batch: int, rows: int, cols: int):
 
 
 def requant_transpose_mxfp8_sr(codes, scales, tensor_scale, batch: int, rows: int, cols: int,
-                               seed: int):
-    """NVFP4 [rows][cols] -> transposed MXFP8 [cols][rows] with stochastic rounding."""
+                               seed: int, first: int = 0):
+    """NVFP4 [rows][cols] -> transposed MXFP8 [cols][rows] with stochastic rounding;
+    `first` as in requant_transpose_sr."""
     c, s = _np(codes, np.uint8), _np(scales, np.uint8)
     ts = _np(tensor_scale, np.float32)
     n = batch * rows * cols
@@ -288,7 +292,7 @@ def requant_transpose_mxfp8_sr(codes, scales, tensor_scale, batch: int, rows: in
     tst = np.zeros(batch, np.float32)
     lib().tqo_requant_transpose_mxfp8_sr(_ptr(c), _ptr(s), _ptr(ts), batch, rows, cols,
                                          C.c_uint64(seed & (2 ** 64 - 1)), _ptr(ct), _ptr(st),
-                                         _ptr(tst))
+                                         _ptr(tst), int(first))
     return {"codes": ct, "scales": st, "tensor_scale": tst}
 
 

@@ -422,12 +422,14 @@ int tqo_sr_index(float a, int k)
  * 3. y = u * r', m = SR index of |y| with the element's random byte, sign as Q.
  * 4. The tensor scale is copied.
  * Random byte: element (b, j, r) of the output has linear index
- * i = (b * cols + j) * rows + r.
+ * i = (b * cols + j) * rows + r.  `first` is the index of tensor 0 of this call
+ * within a larger batch, so one tensor of a batch can be recomputed alone: the
+ * random bytes use i + first * cols * rows, the outputs are written from 0.
  */
 void tqo_requant_transpose_sr(const uint8_t *codes, const uint8_t *scales,
                               const float *tensor_scale, int64_t batch, int64_t rows,
                               int64_t cols, uint64_t seed, uint8_t *codes_t, uint8_t *scales_t,
-                              float *tensor_scale_t)
+                              float *tensor_scale_t, int64_t first)
 {
     const int64_t per_tensor = rows * cols;
     for (int64_t b = 0; b < batch; ++b) {
@@ -453,12 +455,13 @@ void tqo_requant_transpose_sr(const uint8_t *codes, const uint8_t *scales,
                 float dec_new = (float)tqo_e4m3_value(e_new);
                 for (int q = 0; q < 16; ++q) {
                     int64_t i = (b * cols + j) * rows + 16 * t + q; /* output linear index */
+                    int64_t gi = ((first + b) * cols + j) * rows + 16 * t + q; /* in the whole batch */
                     int m = 0;
                     float y = 0.0f;
                     if (dec_new != 0.0f) {
                         float rr = 1.0f / dec_new;
                         y = u[q] * rr;
-                        m = tqo_sr_index(fabsf(y), tqo_sr_byte(seed, (uint64_t)i));
+                        m = tqo_sr_index(fabsf(y), tqo_sr_byte(seed, (uint64_t)gi));
                     }
                     int s = (y < 0.0f && m != 0) ? 1 : 0;
                     put_code(codes_t, i, 8 * s + m);
@@ -658,13 +661,14 @@ int tqo_e4m3_sr(float a, int k)
  * stochastic rounding; forward/backward-mismatch paragraph).  Per new block:
  * se = shared exponent of max|u|, y = u * 2^-se (exact), code = sign | E4M3 SR
  * of |y| with the element's random byte (the stream of tqo_sr_byte at output
- * index i = (b * cols + j) * rows + r).  The tensor scale is copied.
+ * index i = (b * cols + j) * rows + r, offset by first * cols * rows as in
+ * tqo_requant_transpose_sr).  The tensor scale is copied.
  * Requires rows % 32 == 0, cols % 16 == 0.  codes_t [batch][cols][rows],
  * scales_t [batch][cols][rows/32]. */
 void tqo_requant_transpose_mxfp8_sr(const uint8_t *codes, const uint8_t *scales,
                                     const float *tensor_scale, int64_t batch, int64_t rows,
                                     int64_t cols, uint64_t seed, uint8_t *codes_t,
-                                    uint8_t *scales_t, float *tensor_scale_t)
+                                    uint8_t *scales_t, float *tensor_scale_t, int64_t first)
 {
     const int64_t per_tensor = rows * cols;
     for (int64_t b = 0; b < batch; ++b) {
@@ -684,6 +688,7 @@ void tqo_requant_transpose_mxfp8_sr(const uint8_t *codes, const uint8_t *scales,
                 }
                 const int64_t si = (b * cols + j) * (rows / 32) + t;
                 const int64_t o = (b * cols + j) * rows + 32 * t;
+                const int64_t go = ((first + b) * cols + j) * rows + 32 * t; /* in the whole batch */
                 if (A == 0.0f) {
                     scales_t[si] = 0;
                     for (int q = 0; q < 32; ++q)
@@ -694,7 +699,7 @@ void tqo_requant_transpose_mxfp8_sr(const uint8_t *codes, const uint8_t *scales,
                 scales_t[si] = (uint8_t)(se + 127);
                 for (int q = 0; q < 32; ++q) {
                     float y = ldexpf(u[q], -se);
-                    int m = tqo_e4m3_sr(fabsf(y), tqo_sr_byte(seed, (uint64_t)(o + q)));
+                    int m = tqo_e4m3_sr(fabsf(y), tqo_sr_byte(seed, (uint64_t)(go + q)));
                     codes_t[o + q] = (uint8_t)((y < 0.0f && m != 0) ? (0x80 | m) : m);
                 }
             }

@@ -434,6 +434,24 @@ def test_mxfp8_sr_transpose_full_size():
     assert np.array_equal(npu8(t.scales), ot["scales"])
 
 
+
+def test_mxfp8_sr_transpose_moe_layer():
+    """One MoE layer per call (64 experts of [2048 x 768], 3072 tiles), the launch the
+    MXFP8 backward copy of the expert weights takes; sampled experts bit-exact against
+    the oracle, recomputed alone with their index in the batch."""
+    B, R, Cc = 64, 2048, 768
+    c, s, ts = inputs.random_nvfp4(B, R, Cc, seed=31, device=DEV, zero_block_frac=0.02)
+    q = ops.NVFP4(c, s, ts, torch.zeros(B, device=DEV))
+    t = ops.requant_transpose_mxfp8_sr(q, B, R, Cc, seed=47)
+    torch.cuda.synchronize()
+    per = R * Cc
+    for b in [0, 31, B - 1]:
+        o = oracle.requant_transpose_mxfp8_sr(npu8(c[b]), npu8(s[b]), npu8(ts[b:b + 1]),
+                                              1, R, Cc, 47, first=b)
+        assert np.array_equal(npu8(t.codes.reshape(-1)[b * per:(b + 1) * per]), o["codes"]), f"expert {b}"
+        assert np.array_equal(npu8(t.scales.reshape(-1)[b * per // 32:(b + 1) * per // 32]), o["scales"])
+
+
 # ----------------------------------------------------------------------------------
 # 16x16-tile scaling
 # ----------------------------------------------------------------------------------
@@ -513,6 +531,30 @@ def test_transpose_sr_full_size():
     assert np.array_equal(npu8(t0.codes), ot["codes"])
     assert np.array_equal(npu8(t0.scales), ot["scales"])
     assert np.array_equal(npu8(t0.tensor_scale), ot["tensor_scale"])
+
+
+
+def test_transpose_sr_moe_step_launch():
+    """The MoE step's launch: 24 layers x 64 experts of [2048 x 768] in one call
+    (73728 tiles; each workgroup walks nine).  Tensors 0, 777 and 1535 come from the
+    first, a middle and the last tile of their workgroups' walks; bit-exact against
+    the oracle, recomputed alone with their index in the batch, for both seeds the
+    step uses."""
+    B, R, Cc = 24 * 64, 2048, 768
+    c, s, ts = inputs.random_nvfp4(B, R, Cc, seed=29, device=DEV, zero_block_frac=0.02)
+    q = ops.NVFP4(c, s, ts, torch.zeros(B, device=DEV))
+    per = R * Cc
+    for seed in [0, 1]:
+        t = ops.requant_transpose_sr(q, B, R, Cc, seed=seed)
+        torch.cuda.synchronize()
+        for b in [0, 777, B - 1]:
+            o = oracle.requant_transpose_sr(npu8(c[b]), npu8(s[b]), npu8(ts[b:b + 1]),
+                                            1, R, Cc, seed, first=b)
+            got = npu8(t.codes.reshape(-1)[b * per // 2:(b + 1) * per // 2])
+            assert np.array_equal(got, o["codes"]), f"seed {seed} tensor {b}"
+            got = npu8(t.scales.reshape(-1)[b * per // 16:(b + 1) * per // 16])
+            assert np.array_equal(got, o["scales"]), f"seed {seed} tensor {b}"
+            assert npu8(t.tensor_scale[b:b + 1])[0] == o["tensor_scale"][0]
 
 
 SR_SHAPES = [(1, 16, 16), (1, 48, 80), (3, 272, 96), (2, 16, 1040), (1, 32, 64), (2, 528, 144),

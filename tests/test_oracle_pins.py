@@ -548,6 +548,28 @@ def test_sr_on_grid_is_exact_transpose(orc):
     assert (dq_out.reshape(B, Cc, R) == dq_in.reshape(B, R, Cc).transpose(0, 2, 1)).all()
 
 
+def test_sr_first_tensor_offset(orc):
+    """One tensor of a batch recomputed alone: with `first` = its index the random
+    bytes are those of the whole batch, so both transposes reproduce that tensor's
+    slice of the batch output (and differ from a call without the offset)."""
+    from fp4_quantization_precision_amd import inputs
+    B, R, Cc, b = 3, 64, 48, 2
+    c, s, ts = (t.numpy().reshape(-1) for t in inputs.random_nvfp4(B, R, Cc, seed=23))
+    per = R * Cc
+    cb, sb, tb = c[b * per // 2:(b + 1) * per // 2], s[b * per // 16:(b + 1) * per // 16], ts[b:b + 1]
+    full = orc.requant_transpose_sr(c, s, ts, B, R, Cc, 5)
+    one = orc.requant_transpose_sr(cb, sb, tb, 1, R, Cc, 5, first=b)
+    assert np.array_equal(one["codes"], full["codes"][b * per // 2:(b + 1) * per // 2])
+    assert np.array_equal(one["scales"], full["scales"][b * per // 16:(b + 1) * per // 16])
+    assert not np.array_equal(one["codes"], orc.requant_transpose_sr(cb, sb, tb, 1, R, Cc, 5)["codes"])
+    full = orc.requant_transpose_mxfp8_sr(c, s, ts, B, R, Cc, 5)
+    one = orc.requant_transpose_mxfp8_sr(cb, sb, tb, 1, R, Cc, 5, first=b)
+    assert np.array_equal(one["codes"], full["codes"][b * per:(b + 1) * per])
+    assert np.array_equal(one["scales"], full["scales"][b * per // 32:(b + 1) * per // 32])
+    assert not np.array_equal(one["codes"],
+                              orc.requant_transpose_mxfp8_sr(cb, sb, tb, 1, R, Cc, 5)["codes"])
+
+
 def test_sr_bracket_and_bias(orc):
     """Random stored tensors (zero blocks included): every output code lies in
     the bracket of y = u * r' (exact check with the torch E4M3 cast of A'/6),
