@@ -547,7 +547,7 @@ TRAFFIC = {
     "quantize_hint": {"bytes_per_layer": 270527844, "fetch_kib": 2359333.2, "write_kib": 1622067.2, "layers": 24, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.000
     "guided": {"bytes_per_layer": 270530314, "fetch_kib": 2506846.6, "write_kib": 1327113.3, "layers": 24, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.000
     "mismatch": {"bytes_per_layer": 101033721, "fetch_kib": 1769513.6, "write_kib": 13117.7, "layers": 36, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.004
-    "sr_transpose": {"bytes_per_layer": 131841831, "fetch_kib": 673571.5, "write_kib": 1742967.7, "layers": 24, "sources_sha256": "5625324cbf8ff934e71296f15a91b37b578476b2150a851c9f6d3bd393b7db85"},  # 1.164
+    "sr_transpose": {"bytes_per_layer": 131841831, "fetch_kib": 673571.5, "write_kib": 1742967.7, "layers": 24, "sources_sha256": "ef1c9a3ed9208bc4560fb3129e2aba3223067b9b971d3be6a5096029a8353790"},  # 1.164
     "gemm": {"bytes_per_layer": 159249799, "fetch_kib": 44993.0, "write_kib": 65536.0, "layers": 1, "sources_sha256": "56b93a30f9f2d805d2bcc31c6c0b690b08abbabcc2632fc05ae18bd2c1d89dd8"},  # 1.070
 }
 
