@@ -114,7 +114,10 @@ __global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const void* __restr
 
 constexpr int kMTR = 128, kMTC = 256, kMThreads = 512, kMLdsStride = 68;
 
-__device__ __forceinline__ int mlds_slot(int c, int p) { return c * kMLdsStride + (p ^ (8 * (c >> 5))); }
+// LDS dword of tile column c, input row pair p: the row pair XOR 4 * chunk puts each
+// half-wave's 32 stores of the load phase on 32 distinct banks (stores are served 32
+// lanes at a time over 32 banks; c * 68 is one bank for all lanes of an instruction).
+__device__ __forceinline__ int mlds_slot(int c, int p) { return c * kMLdsStride + (p ^ (4 * (c >> 5))); }
 
 // Persistent: each workgroup walks a strided list of tiles and loads the next
 // tile's codes and scales while it requantizes the current one.  WIDE: tile
@@ -232,9 +235,10 @@ __global__ __launch_bounds__(kMThreads, 2) void requant_transpose_mxfp8_sr_kerne
                     uint32_t pk[16];
 #pragma unroll
                     for (int part = 0; part < 2; ++part) {
-                        const uint4* src = reinterpret_cast<const uint4*>(
-                            u_s + c * kMLdsStride + 8 * ((4 * half + 2 * q + part) ^ h));
-                        const uint4 v0 = src[0], v1 = src[1];
+                        // row pairs 8X .. 8X+7 sit at 8 (X ^ (h >> 1)) + (t ^ 4 (h & 1))
+                        const uint32_t* blk = u_s + c * kMLdsStride + 8 * ((4 * half + 2 * q + part) ^ (h >> 1));
+                        const uint4 v0 = *reinterpret_cast<const uint4*>(blk + 4 * (h & 1));
+                        const uint4 v1 = *reinterpret_cast<const uint4*>(blk + 4 * ((h & 1) ^ 1));
                         pk[8 * part + 0] = v0.x; pk[8 * part + 1] = v0.y;
                         pk[8 * part + 2] = v0.z; pk[8 * part + 3] = v0.w;
                         pk[8 * part + 4] = v1.x; pk[8 * part + 5] = v1.y;

@@ -17,10 +17,11 @@
 // dequantizes them exactly with gfx950's packed FP4 -> f32 conversion
 // (u = +-G[m] * dec(e) has at most 6 significant bits, so bf16 holds it) and
 // stores each column's two values as one dword into LDS, where tile column c
-// (= output row) is an LDS row.  The row-pair index is XOR-swizzled by the
-// column's chunk so that the stores of a wave hit distinct banks, and the LDS
-// row pitch is 68 dwords so that the 16-byte reads of the next phase are
-// conflict-free as well.
+// (= output row) is an LDS row.  The row-pair index is XOR-swizzled with four
+// times the column's chunk so that each half-wave's stores hit 32 distinct
+// banks, and the LDS row pitch is 68 dwords so that the 16-byte reads of the
+// next phase are conflict-free as well (their two halves swap places for odd
+// chunks).
 //
 // Requantize phase: a thread owns one output row and four new 16-element
 // blocks: block amax, E4M3 scale, one Philox4x32-10 call for the block's 16
@@ -46,8 +47,12 @@ constexpr int kTC = 256;          // input columns per tile (= output rows)
 constexpr int kSThreads = 512;
 constexpr int kLdsStride = 68;    // dwords per LDS row: 64 row pairs + 4 pad
 
-// LDS dword of tile column c, input row pair p
-__device__ __forceinline__ int lds_slot(int c, int p) { return c * kLdsStride + (p ^ (8 * (c >> 5))); }
+// LDS dword of tile column c, input row pair p.  LDS stores are served 32 lanes at a
+// time over 32 four-byte banks.  A store instruction of the load phase has one
+// column offset within each lane's 32-column chunk, so c * 68 is the same bank for
+// every lane, and the row pair XOR 4 * chunk puts the 32 lanes of each half-wave
+// (four row pairs x eight chunks) on 32 distinct banks.
+__device__ __forceinline__ int lds_slot(int c, int p) { return c * kLdsStride + (p ^ (4 * (c >> 5))); }
 
 // Stochastic rounding of eight values with their random bytes k[0..7]: floor
 // codes from the hardware truncation (saturating at 6), plus one where the
@@ -217,8 +222,10 @@ __global__ __launch_bounds__(kSThreads, 2) void requant_transpose_sr_kernel(
                     if (lr >= rows_valid)
                         continue;
                     ++nvalid;
-                    const uint4* src = reinterpret_cast<const uint4*>(u_s + c * kLdsStride + 8 * ((4 * half + q) ^ h));
-                    const uint4 v0 = src[0], v1 = src[1];
+                    // row pairs 8X .. 8X+7 of the block sit at 8 (X ^ (h >> 1)) + (t ^ 4 (h & 1))
+                    const uint32_t* blk = u_s + c * kLdsStride + 8 * ((4 * half + q) ^ (h >> 1));
+                    const uint4 v0 = *reinterpret_cast<const uint4*>(blk + 4 * (h & 1));
+                    const uint4 v1 = *reinterpret_cast<const uint4*>(blk + 4 * ((h & 1) ^ 1));
                     const uint32_t pk[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
                     float u[16];
 #pragma unroll
