@@ -10,7 +10,7 @@
 // [-127, 127]; elements saturate at 448; zero is +0.
 //
 // Quantize: one lane per 32-value block (64 bytes of bf16 in, 32 code bytes and
-// one scale byte out).  Transpose: tiles of 128 input rows x 256 input columns
+// one scale byte out), E4M3 bytes from the packed hardware conversion.  Transpose: tiles of 128 input rows x 256 input columns
 // staged through LDS exactly as in the NVFP4 transpose; each thread then owns
 // one output row and two new blocks of 32 (its 64 values of the tile), with
 // two Philox4x32-10 calls per block for the 32 random bytes.
@@ -32,11 +32,23 @@ __device__ __forceinline__ int mx_shared_exp(float A)
     return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-// E4M3 byte of y: nearest, ties to even, saturating at 448, zero as +0.
-__device__ __forceinline__ uint32_t e4m3_signed_nearest(float y)
+// E4M3 bytes of y0..y3 (little-endian in one word): nearest, ties to even, saturating
+// at 448, zero as +0, from gfx950's packed f32 -> E4M3 conversion (scale 1).  A device
+// check over every finite binary32 input found the conversion equal to that rule for
+// |y| <= 448, except that it writes -0 (0x80) for negative values that round to zero,
+// and NaN for |y| > 448.  So the values are clamped to +-448 first (the rule's
+// saturation), and the sign bit of zero bytes is cleared: bit 7 of a byte is kept iff
+// its low seven bits are nonzero (their sum with 0x7F carries into bit 7).
+__device__ __forceinline__ uint32_t e4m3x4_nearest(float y0, float y1, float y2, float y3)
 {
-    const uint32_t m = e4m3_encode(fabsf(y));
-    return (y < 0.0f && m != 0u) ? (0x80u | m) : m;
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    auto clamp = [](float y) { return __builtin_amdgcn_fmed3f(y, -448.0f, 448.0f); };
+    s16x2 r = {0, 0};
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, clamp(y0), clamp(y1), 1.0f, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, clamp(y2), clamp(y3), 1.0f, true);
+    const uint32_t w = __builtin_bit_cast(uint32_t, r);
+    const uint32_t nz = (w & 0x7F7F7F7Fu) + 0x7F7F7F7Fu;
+    return w & (nz | 0x7F7F7F7Fu);
 }
 
 // E4M3 stochastic rounding of a >= 0 with random byte k: floor grid point from
@@ -103,8 +115,9 @@ __global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const void* __restr
             const int se = mx_shared_exp(A);
             sb = (uint32_t)(se + 127);
 #pragma unroll
-            for (int i = 0; i < 32; ++i)
-                w[i >> 2] |= e4m3_signed_nearest(__builtin_ldexpf(v[i], -se)) << (8 * (i & 3));
+            for (int i = 0; i < 8; ++i)
+                w[i] = e4m3x4_nearest(__builtin_ldexpf(v[4 * i], -se), __builtin_ldexpf(v[4 * i + 1], -se),
+                                      __builtin_ldexpf(v[4 * i + 2], -se), __builtin_ldexpf(v[4 * i + 3], -se));
         }
         codes[2 * blk] = make_uint4(w[0], w[1], w[2], w[3]);
         codes[2 * blk + 1] = make_uint4(w[4], w[5], w[6], w[7]);

@@ -378,6 +378,13 @@ def test_mxfp8_quantize_shapes(shape):
     x[rng.random(x.shape) < 0.01] *= 1000
     x.reshape(-1)[:32] = 0.0                     # an all-zero block
     x.reshape(-1)[32:64] *= 2.0 ** -120           # a block near the bottom of the range
+    if x.size >= 96:
+        # shared exponent 0: saturation at 448 from above, negative values that round to
+        # zero (written +0), -0, ties to even in the normal and subnormal ranges, the
+        # smallest subnormal (all exact in bf16 too)
+        edge = [480.0, -464.0, 456.0, -2.0 ** -11, -2.0 ** -10, -3 * 2.0 ** -11, 0.0, -0.0,
+                1.0625, 1.1875, -1.0625, 3 * 2.0 ** -10, -2.0 ** -9, 2.0 ** -7 + 2.0 ** -10, 448.0, -448.0]
+        x.reshape(-1)[64:96] = np.float32(edge + edge[::-1])
     xt = torch.from_numpy(x)
     if dt == "bf16":
         xt = xt.to(torch.bfloat16)
