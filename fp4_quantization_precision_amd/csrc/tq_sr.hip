@@ -54,6 +54,30 @@ constexpr int kLdsStride = 68;    // dwords per LDS row: 64 row pairs + 4 pad
 // (four row pairs x eight chunks) on 32 distinct banks.
 __device__ __forceinline__ int lds_slot(int c, int p) { return c * kLdsStride + (p ^ (4 * (c >> 5))); }
 
+// New block scale from the block maximum A (0, or at least 2^-10: a nonzero |u| is
+// G[m] * dec(e) >= 0.5 * 2^-9).  The three steps give the bits of the plain forms
+// e4m3_encode(A / 6), e4m3_decode and 1 / dec, each checked on the device over its whole
+// domain here: A / 6 as A * RN(1/6) with one FMA correction equals the correctly rounded
+// quotient for every finite A >= 2^-125 (and 0); the packed f32 -> E4M3 conversion
+// equals the nearest rule for 0 <= d <= 448 (the minimum with 448 gives the rule's
+// saturation); v_rcp_f32 with one Newton step equals the correctly rounded reciprocal of
+// all 126 nonzero finite E4M3 values.  d = 0 keeps rcp = 1 (the codes are then zero).
+struct BlockScale { uint32_t e; float dec, rcp; };
+__device__ __forceinline__ BlockScale block_scale(float A)
+{
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    constexpr float kSixth = 1.0f / 6.0f;
+    const float q0 = A * kSixth;
+    const float d = __builtin_fmaf(__builtin_fmaf(-q0, 6.0f, A), kSixth, q0);
+    s16x2 r = {0, 0};
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, fminf(d, 448.0f), 0.0f, 1.0f, false);
+    const uint32_t e = __builtin_bit_cast(uint32_t, r) & 0xFFu;
+    const float dec = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(e, 1.0f, false)[0];
+    const float dd = dec == 0.0f ? 1.0f : dec;
+    const float r0 = __builtin_amdgcn_rcpf(dd);
+    return {e, dec, __builtin_fmaf(__builtin_fmaf(-dd, r0, 1.0f), r0, r0)};
+}
+
 // Stochastic rounding of eight values with their random bytes k[0..7]: floor
 // codes from the hardware truncation (saturating at 6), plus one where the
 // random byte falls below the distance to the floor point, except from the top
@@ -237,10 +261,9 @@ __global__ __launch_bounds__(kSThreads, 2) void requant_transpose_sr_kernel(
 #pragma unroll
                     for (int i = 0; i < 16; ++i)
                         A = fmaxf(A, fabsf(u[i]));
-                    const uint32_t e = e4m3_encode(A / 6.0f);
-                    sc |= e << (8 * q);
-                    const float dec = e4m3_decode(e);
-                    const float rcp = 1.0f / (dec == 0.0f ? 1.0f : dec);
+                    const BlockScale bs = block_scale(A);
+                    sc |= bs.e << (8 * q);
+                    const float dec = bs.dec, rcp = bs.rcp;
                     const uint64_t beta = (uint64_t)(((b * cols + oc) * rows + r0 + lr) / 16);
                     const u32x4 rnd = philox4x32_10((uint32_t)beta, (uint32_t)(beta >> 32), 0u, 0u,
                                                     seed_lo, seed_hi);
