@@ -197,6 +197,8 @@ __global__ __launch_bounds__(kSThreads, 2) void requant_transpose_sr_kernel(
     };
     LRegs R;
     load(blockIdx.x, R);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the first tile is needed at once, and no load
+                                         // is then pending where the loop begins
     for (int64_t idx = blockIdx.x; idx < total_tiles; idx += gridDim.x) {
         const Tile T = tile_of(idx);
         const int64_t b = T.b, r0 = T.r0, c0 = T.c0;
@@ -235,10 +237,14 @@ __global__ __launch_bounds__(kSThreads, 2) void requant_transpose_sr_kernel(
         {
             const int c = tid & (kTC - 1), half = tid >> 8, h = c >> 5;
             const int64_t oc = c0 + c;
-            if (c < cols_valid) {
-                uint32_t out[8];
-                uint32_t sc = 0;
-                int nvalid = 0;
+            // Lanes past the tile's columns compute on the zeros staged there and store
+            // nothing; no branch encloses the computation, so the wait below is on
+            // every path.
+            const bool active = c < cols_valid;
+            uint32_t out[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            uint32_t sc = 0;
+            int nvalid = 0;
+            {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int lr = 64 * half + 16 * q;  // first local input row of the block
@@ -279,6 +285,12 @@ __global__ __launch_bounds__(kSThreads, 2) void requant_transpose_sr_kernel(
                         out[2 * q + 1] = sr_pack8(yc + 8, k + 8);
                     }
                 }
+            }
+            // The next tile's codes were loaded before this phase and have landed.  Waiting
+            // for them here, on every path and before the stores, keeps the next dequant
+            // from waiting on this tile's stores: the vector memory counter covers both.
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            if (active) {
                 uint8_t* orow = codes_t + ((b * cols + oc) * rows + r0 + 64 * half) / 2;
                 uint8_t* srow = scales_t + (b * cols + oc) * sct_pitch + (r0 + 64 * half) / 16;
                 if (nvalid == 4 && vec_out) {
