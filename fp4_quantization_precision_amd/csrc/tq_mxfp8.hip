@@ -211,9 +211,10 @@ __global__ __launch_bounds__(kMThreads, 2) void requant_transpose_mxfp8_sr_kerne
             const int p = lp, cl = lcl;
             float d[2][2];
 #pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {
-                d[rr][0] = e4m3_decode(R.s[rr] & 0xFFu);
-                d[rr][1] = e4m3_decode((R.s[rr] >> 8) & 0xFFu);
+            for (int rr = 0; rr < 2; ++rr) {  // both scale bytes by the exact E4M3 decode
+                const tq_f32x2 dd = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(R.s[rr], 1.0f, false);
+                d[rr][0] = dd[0];
+                d[rr][1] = dd[1];
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
