@@ -547,7 +547,7 @@ TRAFFIC = {
     "quantize_hint": {"bytes_per_layer": 270527950, "fetch_kib": 2359333.4, "write_kib": 1622066.5, "layers": 24, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.000
     "guided": {"bytes_per_layer": 270530731, "fetch_kib": 2506850.4, "write_kib": 1327112.3, "layers": 24, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.000
     "mismatch": {"bytes_per_layer": 101033772, "fetch_kib": 1769513.4, "write_kib": 13117.7, "layers": 36, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.004
-    "sr_transpose": {"bytes_per_layer": 135175406, "fetch_kib": 674191.8, "write_kib": 1819857.0, "layers": 24, "sources_sha256": "94afdc088666fd1a4a9e0f56596d1ded7dd4f08a0c22698d43d67a0bcf88cbba"},  # 1.194
+    "sr_transpose": {"bytes_per_layer": 135175406, "fetch_kib": 674191.8, "write_kib": 1819857.0, "layers": 24, "sources_sha256": "eac8271f5410576433458a8d725da328e8b742bdd99a233b77055ff5c6fc8f42"},  # 1.194
     "gemm": {"bytes_per_layer": 159158219, "fetch_kib": 44948.2, "write_kib": 65536.0, "layers": 1, "sources_sha256": "56b93a30f9f2d805d2bcc31c6c0b690b08abbabcc2632fc05ae18bd2c1d89dd8"},  # 1.069
 }
 

@@ -34,9 +34,9 @@ __device__ __forceinline__ int mx_shared_exp(float A)
 
 // E4M3 bytes of y0..y3 (little-endian in one word): nearest, ties to even, saturating
 // at 448, zero as +0, from gfx950's packed f32 -> E4M3 conversion (scale 1).  A device
-// check over every finite binary32 input found the conversion equal to that rule for
-// |y| <= 448, except that it writes -0 (0x80) for negative values that round to zero,
-// and NaN for |y| > 448.  So the values are clamped to +-448 first (the rule's
+// check over every finite binary32 input finds the conversion equal to that rule for
+// |y| <= 464, except that it writes -0 (0x80) for negative values that round to zero,
+// and NaN above 464.  So the values are clamped to +-448 first (the rule's
 // saturation), and the sign bit of zero bytes is cleared: bit 7 of a byte is kept iff
 // its low seven bits are nonzero (their sum with 0x7F carries into bit 7).
 __device__ __forceinline__ uint32_t e4m3x4_nearest(float y0, float y1, float y2, float y3)

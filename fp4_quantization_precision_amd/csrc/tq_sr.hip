@@ -59,8 +59,9 @@ __device__ __forceinline__ int lds_slot(int c, int p) { return c * kLdsStride + 
 // e4m3_encode(A / 6), e4m3_decode and 1 / dec, each checked on the device over its whole
 // domain here: A / 6 as A * RN(1/6) with one FMA correction equals the correctly rounded
 // quotient for every finite A >= 2^-125 (and 0); the packed f32 -> E4M3 conversion
-// equals the nearest rule for 0 <= d <= 448 (the minimum with 448 gives the rule's
-// saturation); v_rcp_f32 with one Newton step equals the correctly rounded reciprocal of
+// equals the nearest rule for 0 <= d <= 464 and gives NaN above (the minimum with 448
+// gives the rule's saturation); v_rcp_f32 with one Newton step equals the correctly
+// rounded reciprocal of
 // all 126 nonzero finite E4M3 values.  d = 0 keeps rcp = 1 (the codes are then zero).
 struct BlockScale { uint32_t e; float dec, rcp; };
 __device__ __forceinline__ BlockScale block_scale(float A)
