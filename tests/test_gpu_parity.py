@@ -565,7 +565,10 @@ def test_transpose_sr_moe_step_launch():
 
 
 SR_SHAPES = [(1, 16, 16), (1, 48, 80), (3, 272, 96), (2, 16, 1040), (1, 32, 64), (2, 528, 144),
-             (1, 256, 64), (1, 1024, 1024)]
+             (1, 256, 64), (1, 1024, 1024),
+             # 900 tiles, ragged in both directions, on 512 workgroups: workgroups walk one or
+             # two tiles, prefetching partial tiles after full ones and the reverse
+             (100, 272, 528)]
 
 
 @pytest.mark.parametrize("shape", SR_SHAPES)
