@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
     const float* __restrict__ a_tensor_scale, const int32_t* __restrict__ group_offsets,
     int num_groups, int64_t m_total, int64_t n, int64_t k, const uint8_t* __restrict__ w_codes,
     const uint8_t* __restrict__ w_scales, const float* __restrict__ w_tensor_scale,
-    uint16_t* __restrict__ out, int n_tiles)
+    uint16_t* __restrict__ out, int n_tiles, int sw_l2d)
 {
     // Two activation tiles (the one being read, the one being filled), then the
     // staged scales; the output tile is staged over the same bytes.
@@ -333,7 +333,8 @@ __global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
     // SLDS: copy the tile's block scales (rows x K/16 bytes, contiguous and
     // 16-byte aligned) into LDS with 16-byte loads; loads past the tile's rows
     // read zeros.
-    auto copy_scales = [&](__amdgpu_buffer_rsrc_t rs, int bytes, uint8_t* dst, auto cap) __attribute__((always_inline)) {
+    // l2d >= 0: rows of D = 2^l2d dwords, dword w of row r stored at w ^ rot(r) (see wrot)
+    auto copy_scales = [&](__amdgpu_buffer_rsrc_t rs, int bytes, uint8_t* dst, auto cap, int l2d) __attribute__((always_inline)) {
         constexpr int kRounds = decltype(cap)::value / (16 * kGThreads);
         uint4 v[kRounds];
 #pragma unroll
@@ -342,12 +343,34 @@ __global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
                 v[u] = to_uint4(__builtin_amdgcn_raw_buffer_load_b128(rs, 16 * (tid + kGThreads * u), 0, 0));
 #pragma unroll
         for (int u = 0; u < kRounds; ++u)
-            if (u * 16 * kGThreads < bytes)
-                *reinterpret_cast<uint4*>(dst + 16 * (tid + kGThreads * u)) = v[u];
+            if (u * 16 * kGThreads < bytes) {
+                if (l2d < 0) {
+                    *reinterpret_cast<uint4*>(dst + 16 * (tid + kGThreads * u)) = v[u];
+                } else {
+                    const uint32_t e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+                    const uint32_t dm = (1u << l2d) - 1u;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t q = 4u * (uint32_t)(tid + kGThreads * u) + (uint32_t)i;
+                        const uint32_t r = q >> l2d, rot = (r >> (5 - l2d)) & dm;
+                        reinterpret_cast<uint32_t*>(dst)[(r << l2d) + ((q & dm) ^ rot)] = e[i];
+                    }
+                }
+            }
     };
     // two scale bytes (blocks 2 q, 2 q + 1 of a 32-k piece) of slice t from a staged row
     auto lds_scales = [&](const uint8_t* rowp, int t, int q) -> uint32_t {
         const uint8_t* p = rowp + kofs(t) / 16 + 2 * q;
+        return (uint32_t)p[0] | ((uint32_t)p[1] << 8);
+    };
+    // Weight scales of slice t for column wcol[j].  With sw_l2d >= 0 (K % 64 == 0 and
+    // K / 64 = D a power of two) the staged rows are rotated: dword w of row r sits at
+    // w ^ ((r >> (5 - l2d)) & (D - 1)), which puts the 32 rows that a half-wave reads
+    // at one slice on 32 distinct banks (rows D dwords apart would otherwise share
+    // 32 / D... banks: all 32 lanes on one bank for K = 2048).
+    auto lds_wscales = [&](int j, int t) -> uint32_t {
+        const int rot = sw_l2d >= 0 ? (wcol[j] >> (5 - sw_l2d)) & ((1 << sw_l2d) - 1) : 0;
+        const uint8_t* p = Ws + wcol[j] * kb + kofs(t) / 16 + 4 * ((t ^ rot) - t) + 2 * h;
         return (uint32_t)p[0] | ((uint32_t)p[1] << 8);
     };
     // blocks of a partial first slice past K % 64 get zero scales
@@ -404,9 +427,9 @@ __global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
         }
         load_w(1, S1);
         if constexpr (SLDS) {
-            copy_scales(rs_s, w_rows * kb, Ws, std::integral_constant<int, kWSTile>{});
+            copy_scales(rs_s, w_rows * kb, Ws, std::integral_constant<int, kWSTile>{}, sw_l2d);
             if constexpr (A_FP4) {
-                copy_scales(rs_as, a_rows * kb, As_s, std::integral_constant<int, kASTile>{});
+                copy_scales(rs_as, a_rows * kb, As_s, std::integral_constant<int, kASTile>{}, -1);
                 __syncthreads();  // store_a reads activation scales other threads copied
             }
         }
@@ -417,7 +440,7 @@ __global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
         if (steps > 0) {
 #pragma unroll
             for (int j = 0; j < kNJ; ++j) {
-                sc[j] = lds_scales(Ws + wcol[j] * kb, 0, h);
+                sc[j] = lds_wscales(j, 0);
                 if (r_tail)
                     sc[j] = mask_partial(sc[j], h);
             }
@@ -440,7 +463,7 @@ __global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
             // next slice's weight scales (past the last slice: of no consequence)
 #pragma unroll
             for (int j = 0; j < kNJ; ++j)
-                sc[j] = lds_scales(Ws + wcol[j] * kb, t + 1 < steps ? t + 1 : t, h);
+                sc[j] = lds_wscales(j, t + 1 < steps ? t + 1 : t);
         }
         auto word = [&](int j, int kk) -> uint32_t {
             return kk == 0 ? cur.w[j].x : (kk == 1 ? cur.w[j].y : (kk == 2 ? cur.w[j].z : cur.w[j].w));
@@ -602,14 +625,19 @@ static void launch_gemm(const void* a, const uint8_t* a_scales, const float* a_t
     bool slds = kb * kBN <= kWSTile && al16(w_scales) && (n * kb) % 16 == 0;
     if (A_FP4)
         slds = slds && kb * kBM <= kASTile && al16(a_scales) && kb % 16 == 0;
+    // staged weight-scale rows rotated when K / 64 is a power of two (see lds_wscales)
+    int sw_l2d = -1;
+    if (k % 64 == 0 && k / 64 <= 32 && ((k / 64) & (k / 64 - 1)) == 0)
+        for (sw_l2d = 0; (1 << sw_l2d) < k / 64; ++sw_l2d) {
+        }
     if (slds)
         hipLaunchKernelGGL((grouped_gemm_nvfp4_kernel<A_FP4, true>), dim3((unsigned)grid),
                            dim3(kGThreads), 0, s, a, a_scales, a_tensor_scale, group_offsets,
-                           num_groups, m_total, n, k, w_codes, w_scales, w_tensor_scale, out, n_tiles);
+                           num_groups, m_total, n, k, w_codes, w_scales, w_tensor_scale, out, n_tiles, sw_l2d);
     else
         hipLaunchKernelGGL((grouped_gemm_nvfp4_kernel<A_FP4, false>), dim3((unsigned)grid),
                            dim3(kGThreads), 0, s, a, a_scales, a_tensor_scale, group_offsets,
-                           num_groups, m_total, n, k, w_codes, w_scales, w_tensor_scale, out, n_tiles);
+                           num_groups, m_total, n, k, w_codes, w_scales, w_tensor_scale, out, n_tiles, sw_l2d);
 }
 
 void launch_grouped_gemm_nvfp4(const uint16_t* a, const int32_t* group_offsets, int num_groups,
