@@ -542,13 +542,13 @@ KERNEL_OF = {
 TRAFFIC = {
     # FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0: the 1 GiB copy read 524314 KiB fetched and
     # 1048576 KiB written.  Ratio to the algorithmic bytes in the comments.
-    "amax": {"bytes_per_layer": 201325939, "fetch_kib": 4718763.2, "write_kib": 96.0, "layers": 48, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.000
-    "quantize": {"bytes_per_layer": 257943897, "fetch_kib": 3538979.2, "write_kib": 1990733.6, "layers": 36, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.000
-    "quantize_hint": {"bytes_per_layer": 270527950, "fetch_kib": 2359333.4, "write_kib": 1622066.5, "layers": 24, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.000
-    "guided": {"bytes_per_layer": 270530731, "fetch_kib": 2506850.4, "write_kib": 1327112.3, "layers": 24, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.000
-    "mismatch": {"bytes_per_layer": 101033772, "fetch_kib": 1769513.4, "write_kib": 13117.7, "layers": 36, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.004
-    "sr_transpose": {"bytes_per_layer": 135175406, "fetch_kib": 674191.8, "write_kib": 1819857.0, "layers": 24, "sources_sha256": "eac8271f5410576433458a8d725da328e8b742bdd99a233b77055ff5c6fc8f42"},  # 1.194
-    "gemm": {"bytes_per_layer": 159158219, "fetch_kib": 44948.2, "write_kib": 65536.0, "layers": 1, "sources_sha256": "56b93a30f9f2d805d2bcc31c6c0b690b08abbabcc2632fc05ae18bd2c1d89dd8"},  # 1.069
+    "amax": {"bytes_per_layer": 201325797, "fetch_kib": 4718757.1, "write_kib": 96.0, "layers": 48, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.000
+    "quantize": {"bytes_per_layer": 257944055, "fetch_kib": 3538979.9, "write_kib": 1990733.5, "layers": 36, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.000
+    "quantize_hint": {"bytes_per_layer": 270528010, "fetch_kib": 2359332.4, "write_kib": 1622067.1, "layers": 24, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.000
+    "guided": {"bytes_per_layer": 270530639, "fetch_kib": 2506847.8, "write_kib": 1327112.6, "layers": 24, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.000
+    "mismatch": {"bytes_per_layer": 101033841, "fetch_kib": 1769513.6, "write_kib": 13117.7, "layers": 36, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.004
+    "sr_transpose": {"bytes_per_layer": 135414149, "fetch_kib": 674280.6, "write_kib": 1825274.2, "layers": 24, "sources_sha256": "eac8271f5410576433458a8d725da328e8b742bdd99a233b77055ff5c6fc8f42"},  # 1.196
+    "gemm": {"bytes_per_layer": 159250907, "fetch_kib": 44993.4, "write_kib": 65536.0, "layers": 1, "sources_sha256": "abb3069352c9fa1487c1f62771151944dd0178fc6deab0bced739799d2e210c1"},  # 1.070
 }
 
 
