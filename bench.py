@@ -548,7 +548,7 @@ TRAFFIC = {
     "guided": {"bytes_per_layer": 270530639, "fetch_kib": 2506847.8, "write_kib": 1327112.6, "layers": 24, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.000
     "mismatch": {"bytes_per_layer": 101033841, "fetch_kib": 1769513.6, "write_kib": 13117.7, "layers": 36, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.004
     "sr_transpose": {"bytes_per_layer": 135414149, "fetch_kib": 674280.6, "write_kib": 1825274.2, "layers": 24, "sources_sha256": "eac8271f5410576433458a8d725da328e8b742bdd99a233b77055ff5c6fc8f42"},  # 1.196
-    "gemm": {"bytes_per_layer": 159250907, "fetch_kib": 44993.4, "write_kib": 65536.0, "layers": 1, "sources_sha256": "abb3069352c9fa1487c1f62771151944dd0178fc6deab0bced739799d2e210c1"},  # 1.070
+    "gemm": {"bytes_per_layer": 159250907, "fetch_kib": 44993.4, "write_kib": 65536.0, "layers": 1, "sources_sha256": "234bcd5a07abdf64d459419c0990277f1f94565dcccbe9d323ff0f877f428939"},  # 1.070
 }
 
 

@@ -366,8 +366,8 @@ __global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
     // Weight scales of slice t for column wcol[j].  With sw_l2d >= 0 (K % 64 == 0 and
     // K / 64 = D a power of two) the staged rows are rotated: dword w of row r sits at
     // w ^ ((r >> (5 - l2d)) & (D - 1)), which puts the 32 rows that a half-wave reads
-    // at one slice on 32 distinct banks (rows D dwords apart would otherwise share
-    // 32 / D... banks: all 32 lanes on one bank for K = 2048).
+    // at one slice on 32 distinct banks.  Unrotated, rows D dwords apart fall on only
+    // 32 / D distinct banks (one bank for all 32 lanes at K = 2048).
     auto lds_wscales = [&](int j, int t) -> uint32_t {
         const int rot = sw_l2d >= 0 ? (wcol[j] >> (5 - sw_l2d)) & ((1 << sw_l2d) - 1) : 0;
         const uint8_t* p = Ws + wcol[j] * kb + kofs(t) / 16 + 4 * ((t ^ rot) - t) + 2 * h;
