@@ -12,15 +12,22 @@ X_t, both resident in HBM.  The step runs in phases, each one kernel over all
   4. trainer guided quantize of X_t with the hints (latter half of the layers)
   5. code-mismatch counts rollout vs trainer (before / after guidance)
   6. dequantize -> transpose -> stochastic-rounding requantize of the trainer's
-     weights (the backward copy), Philox seed = layer
+     weights (the backward copy), Philox seed 0 for the unguided layers and 1
+     for the hinted ones
   7. grouped GEMM: 16384 bf16 token rows, Zipf(1.1) over the 64 experts, times
      the trainer's NVFP4 weights (K = 768, N = 2048), bf16 out
 
 `value` is the step's algorithmic bytes (every input read once, every output
 written once) over the measured step time, in GB/s.  Per-kernel durations
 come from HIP events recorded on the launch stream around each phase of the
-timed steps (phase time / launches).  The CPU oracle is timed on a bounded
-sample of the same work.
+timed steps (phase time / launches).
+
+`configs` holds one row per workload configuration (tiny round trip,
+activations 32768 x 4096, transpose-requantize 8192^2 per seed, grouped GEMM
+32 experts x K 2048 x N 768), timed over back-to-back calls that rotate over
+buffer sets larger than the Infinity Cache; `extras` the rows measured on the step's buffers (W4A4
+GEMM, FP4 KV cache, MXFP8, 16x16 tiles).  The CPU oracle is timed on bounded
+samples of each workload, on one thread and on every usable core.
 
     python bench.py [--gpus 1] [--steps 10] [--warmup 2]
 """
@@ -52,7 +59,21 @@ def parse():
     p.add_argument("--layers", type=int, default=LAYERS)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true",
-                   help="skip the rows measured outside the step (W4A4 GEMM, FP4 KV cache)")
+                   help="skip the rows measured outside the step (W4A4 GEMM, FP4 KV cache, "
+                        "MXFP8, 16x16 tiles)")
+    p.add_argument("--no-configs", action="store_true",
+                   help="skip the per-configuration rows (tiny round trip, activations, "
+                        "8192^2 transpose-requantize, 32-expert grouped GEMM)")
+    p.add_argument("--no-step", action="store_true",
+                   help="skip the timed MoE-weights step (for profiling the other sections; "
+                        "the output line then carries no value)")
+    p.add_argument("--reps", type=int, default=20,
+                   help="timed calls per configuration row (back to back, rotating over "
+                        "buffer sets larger than the Infinity Cache)")
+    p.add_argument("--traffic-from", nargs="+", metavar="DIR",
+                   help="write profiles/hbm_traffic.json from rocprofv3 counter CSVs under DIR "
+                        "(read-request and write-request passes) and exit")
+    p.add_argument("--traffic-section", choices=("step", "configs"), default="step")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one 1 GiB device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -60,22 +81,68 @@ def parse():
 
 def main():
     args = parse()
+    if args.traffic_from:
+        print(json.dumps(traffic_from(args.traffic_from, args.traffic_section)[args.traffic_section]))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the path has no "
                                    "multi-GPU leg (--gpus must be 1)"}))
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    from fp4_quantization_precision_amd import _lib, inputs, ops
-    from fp4_quantization_precision_amd._lib import TQ_AMAX_GIVEN, TQ_BF16
+    from fp4_quantization_precision_amd import _lib
 
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     L = _lib.lib()
     stream = torch.cuda.current_stream()
+
+    line = {
+        "metric": "quantize/guided-quantize GB/s and % of HBM peak; grouped-GEMM TFLOP/s",
+        "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+    }
+    step = None
+    if not args.no_step:
+        step = measure_step(args, L, dev, stream)
+        line.update(step["line"])
+    else:
+        line["config"] = {"workload": "per-configuration rows only (no step)"}
+    configs = None if args.no_configs else measure_configs(L, dev, stream, args.reps)
+    extras = None
+    if step is not None and not args.no_extras:
+        extras = measure_extras(L, dev, stream, *step["extras_args"])
+    cpu = None
+    if step is not None and not args.no_cpu_baseline:
+        cpu = cpu_baseline(*step["cpu_args"])
+    line["cpu_baseline"] = cpu
+    line["configs"] = configs
+    line["extras"] = extras
+    if args.copy_calibration:
+        # one plain device copy of 1 GiB (read 1 GiB, write 1 GiB): a yardstick of
+        # known size for the HBM byte counters of the kernels above
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    print(json.dumps(line), flush=True)
+
+
+def measure_step(args, L, dev, stream):
+    """The timed MoE-weights step (all rows of the hot path over the 48-layer
+    workload).  Returns the output-line fields and the buffers the extras and the
+    CPU baseline reuse."""
+    import numpy as np
+    import torch
+
+    from fp4_quantization_precision_amd import inputs, ops
+    from fp4_quantization_precision_amd._lib import TQ_AMAX_GIVEN, TQ_BF16
+
     sp = C.c_void_p(stream.cuda_stream)
     P = lambda t: C.c_void_p(t.data_ptr()) if t is not None else None
 
@@ -232,8 +299,8 @@ def main():
     kernels = {}
     for cat in cat_ms:
         us = 1e3 * cat_ms[cat] / (cat_n[cat] * args.steps)
-        ent = {"launches_per_step": cat_n[cat], "layers_per_launch": cat_layers[cat] / cat_n[cat],
-               "avg_us": round(us, 2)}
+        ent = {"kernel": KERNEL_OF[cat][0], "launches_per_step": cat_n[cat],
+               "layers_per_launch": cat_layers[cat] / cat_n[cat], "avg_us": round(us, 2)}
         if cat == "gemm":
             ent["TFLOP/s"] = round(gemm_flops / (us * 1e-6) / 1e12, 1)
             ent["frac_bf16_mfma_peak"] = round(ent["TFLOP/s"] / BF16_MFMA_PEAK_TFLOPS, 4)
@@ -250,19 +317,9 @@ def main():
         mism["hinted_layers_nearest_rate"] = float(cnt[0, first_hint:, 0].sum() / (nh * n_layer))
         mism["hinted_layers_guided_rate"] = float(cnt[1, first_hint:, 0].sum() / (nh * n_layer))
 
-    if args.copy_calibration:
-        # one plain device copy of 1 GiB (read 1 GiB, write 1 GiB): the yardstick
-        # for the HBM byte counters (FETCH_SIZE / WRITE_SIZE) of the kernels above
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
     # the roofline is reported for the kernel with the largest share of the step
     dom_cat = max(kernels, key=lambda c: kernels[c]["share_of_step"])
     dom = kernels[dom_cat]
-    kname = KERNEL_OF[dom_cat][0]
     if dom_cat == "gemm":
         roofline = {"bound": "mfma", "achieved": dom["TFLOP/s"], "peak": BF16_MFMA_PEAK_TFLOPS,
                     "unit": "TFLOP/s", "frac": dom["frac_bf16_mfma_peak"]}
@@ -270,31 +327,15 @@ def main():
         roofline = {"bound": "hbm", "achieved": dom["GB/s"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": dom["frac_hbm_peak"]}
     roofline.update({"traffic": measured_traffic(dom_cat, dom["layers_per_launch"]),
-                     "kernel": kname, "category": dom_cat,
+                     "kernel": dom["kernel"], "category": dom_cat,
                      "algorithmic_bytes_per_launch": call_bytes(dom_cat),
                      "avg_launch_us": dom["avg_us"], "share_of_step": dom["share_of_step"]})
     if dom_cat == "gemm":
         roofline["algorithmic_flops_per_launch"] = gemm_flops
 
-    extras = None if args.no_extras else measure_extras(L, dev, stream, A, OFF, QG, QN, nl, first_hint)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(XR, XT, A, counts, first_hint)
-
-    line = {
-        "metric": "quantize/guided-quantize GB/s and % of HBM peak; grouped-GEMM TFLOP/s",
+    fields = {
         "value": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 3),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
         "config": {"workload": f"moe-expert-weights {nl}x{EXPERTS}x[{ROWS}x{COLS}] bf16 "
                                f"(rollout+trainer copies; hints for layers >= {first_hint}; "
                                f"SR transpose; grouped GEMM {TOKENS} tokens/layer)",
@@ -305,27 +346,234 @@ def main():
         "step_gemm_tflops": round(step_flops / (ms_per_step * 1e-3) / 1e12, 1),
         "event_ms_per_step": round(ev_step_ms, 3),
         "roofline": roofline,
-        "cpu_baseline": cpu,
         "kernels": kernels,
-        "extras": extras,
         "mismatch": mism,
         "input_generation_s": round(t_gen, 1),
     }
-    print(json.dumps(line), flush=True)
+    return {"line": fields,
+            "extras_args": (A, OFF, QG, QN, nl, first_hint),
+            "cpu_args": (XR, XT, A, counts, first_hint)}
 
 
-def _time_phase(stream, fn, reps):
-    """Average event time (us) of `reps` back-to-back calls of fn on `stream`."""
+def _time_rotating(stream, call, n_sets, reps):
+    """Average event time (us) per call of `reps` back-to-back calls call(i), where
+    call i works on buffer set i % n_sets; the sets together exceed the 256 MiB
+    Infinity Cache, so a call finds little of its input in cache.  One warm-up pass
+    over the sets first; the events are recorded on the launch stream."""
     import torch
-    fn()
-    torch.cuda.synchronize()
+    for i in range(n_sets):
+        call(i)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
     e0.record(stream)
-    for _ in range(reps):
-        fn()
+    for i in range(reps):
+        call(i % n_sets)
     e1.record(stream)
     torch.cuda.synchronize()
-    return 1e3 * e0.elapsed_time(e1) / reps
+    return {"avg_us": round(1e3 * e0.elapsed_time(e1) / reps, 2), "calls": reps, "buffer_sets": n_sets}
+
+
+def _config_traffic(kernel):
+    """Counter-measured HBM bytes per call of a configuration row (the sum over its
+    kernels), or None if not measured on the current sources."""
+    tot = 0
+    for k in kernel.split(" + "):
+        ent = _traffic_entry("configs", k)
+        if ent is None:
+            return None
+        tot += ent["bytes_per_dispatch"]
+    return tot
+
+
+def _bw_row(kernel, timing, alg_bytes, moved_bytes=None, note=None):
+    us = timing["avg_us"]
+    gbs = alg_bytes / us / 1e3
+    row = {"kernel": kernel, **timing, "algorithmic_bytes": alg_bytes, "GB/s": round(gbs, 1),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": _config_traffic(kernel)}}
+    if moved_bytes is not None:
+        row["moved_bytes"] = moved_bytes
+        row["GB/s_moved"] = round(moved_bytes / us / 1e3, 1)
+        row["frac_hbm_peak_moved"] = round(moved_bytes / us / 1e3 / HBM_PEAK_GBS, 4)
+    if note:
+        row["note"] = note
+    return row
+
+
+def _mfma_row(kernel, timing, flops, note=None):
+    us = timing["avg_us"]
+    tf = flops / us / 1e6
+    row = {"kernel": kernel, **timing, "flops": flops, "TFLOP/s": round(tf, 1),
+           "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                        "traffic": _config_traffic(kernel)}}
+    if note:
+        row["note"] = note
+    return row
+
+
+def measure_configs(L, dev, stream, reps):
+    """One row per workload configuration.  Each row times `reps` back-to-back calls
+    with HIP events on the launch stream, rotating over buffer sets that together
+    exceed the 256 MiB Infinity Cache (average per call):
+
+    * tiny round trip, 64 x 256 fp32: the whole chain (launch-bound; no roofline claim);
+    * activations, 32768 x 4096 bf16 (rollout and trainer copies alternate): tensor
+      amax; nearest + hint and guided with the tensor amax given; and tq_quantize from
+      scratch (amax pass + quantize pass);
+    * transpose-requantize of an 8192 x 8192 NVFP4 tensor, one call per seed, over
+      five source tensors;
+    * grouped GEMM, 32 experts, Zipf(1.1) counts over 16384 tokens, K 2048, N 768,
+      over three input sets; and the same with NVFP4 activations."""
+    import torch
+
+    from fp4_quantization_precision_amd import inputs, ops
+    from fp4_quantization_precision_amd._lib import TQ_AMAX_GIVEN, TQ_BF16, TQ_F32
+
+    sp = C.c_void_p(stream.cuda_stream)
+    P = lambda t: C.c_void_p(t.data_ptr()) if t is not None else None
+    out = {}
+
+    def ok(st, what):
+        if st != 0:
+            raise RuntimeError(f"{what}: {L.tq_status_string(st).decode()}")
+
+    # ---- tiny round trip ----
+    xr, xt = (t.to(dev) for t in inputs.tiny_roundtrip())
+    n1 = xr.numel()
+    h1 = torch.empty(ops.hint_words(n1), dtype=torch.int32, device=dev)
+    q1 = [ops.new_nvfp4((1,), 64, 256, dev) for _ in range(3)]
+    c1 = torch.empty((2, 2), dtype=torch.int64, device=dev)
+    pair = torch.empty((2, 2, n1 // 2), dtype=torch.uint8, device=dev)
+
+    def tiny(_):
+        ok(L.tq_quantize(P(xr), TQ_F32, 1, 64, 256, P(q1[0].tensor_amax), P(q1[0].codes),
+                         P(q1[0].scales), P(q1[0].tensor_scale), P(h1), 0, sp), "tiny nearest+hint")
+        ok(L.tq_quantize(P(xt), TQ_F32, 1, 64, 256, P(q1[1].tensor_amax), P(q1[1].codes),
+                         P(q1[1].scales), P(q1[1].tensor_scale), None, 0, sp), "tiny nearest")
+        ok(L.tq_quantize_guided(P(xt), TQ_F32, 1, 64, 256, P(q1[2].tensor_amax), P(h1),
+                                P(q1[2].codes), P(q1[2].scales), P(q1[2].tensor_scale), 0, sp),
+           "tiny guided")
+        ok(L.tq_code_mismatch(P(pair[0]), P(pair[1]), 2, n1, P(c1), sp), "tiny mismatch")
+    t1 = _time_rotating(stream, tiny, 1, reps)
+    out["tiny_roundtrip"] = {
+        "workload": "tiny round trip: 64 x 256 fp32 X_r, X_t = X_r(1+e); nearest + hint, nearest, "
+                    "guided, mismatch counts (7 kernels incl. amax passes and fills)",
+        **t1, "note": "launch-bound; no roofline claim"}
+    del xr, xt, h1, q1, c1, pair
+
+    # ---- activations 32768 x 4096 bf16 ----
+    T3, H3 = 32768, 4096
+    n3 = T3 * H3
+    ar, at, _ = inputs.activations(T3, H3, device=dev)
+    X = (ar, at)
+    hw = ops.hint_words(n3)
+    h3 = [torch.empty(hw, dtype=torch.int32, device=dev) for _ in range(2)]
+    qa = [ops.new_nvfp4((1,), T3, H3, dev) for _ in range(2)]
+    qs = [ops.new_nvfp4((1,), T3, H3, dev) for _ in range(2)]
+    for i in range(2):
+        ok(L.tq_tensor_amax(P(X[i]), TQ_BF16, 1, n3, P(qa[i].tensor_amax), sp), "amax")
+
+    def amax(i):
+        ok(L.tq_tensor_amax(P(X[i]), TQ_BF16, 1, n3, P(qs[i].tensor_amax), sp), "amax")
+
+    def nearest_hint(i):
+        ok(L.tq_quantize(P(X[i]), TQ_BF16, 1, T3, H3, P(qa[i].tensor_amax), P(qa[i].codes),
+                         P(qa[i].scales), P(qa[i].tensor_scale), P(h3[i]), TQ_AMAX_GIVEN, sp),
+           "nearest+hint")
+
+    def guided(i):
+        # the trainer copy guided by the rollout's hints, and (alternating) the reverse
+        ok(L.tq_quantize_guided(P(X[1 - i]), TQ_BF16, 1, T3, H3, P(qa[1 - i].tensor_amax), P(h3[i]),
+                                P(qs[i].codes), P(qs[i].scales), P(qs[i].tensor_scale),
+                                TQ_AMAX_GIVEN, sp), "guided")
+
+    def scratch_hint(i):
+        ok(L.tq_quantize(P(X[i]), TQ_BF16, 1, T3, H3, P(qs[i].tensor_amax), P(qs[i].codes),
+                         P(qs[i].scales), P(qs[i].tensor_scale), P(h3[i]), 0, sp),
+           "from-scratch nearest+hint")
+
+    def scratch(i):
+        ok(L.tq_quantize(P(X[i]), TQ_BF16, 1, T3, H3, P(qs[i].tensor_amax), P(qs[i].codes),
+                         P(qs[i].scales), P(qs[i].tensor_scale), None, 0, sp), "from-scratch nearest")
+    b_q, b_h = n3 * (2 + 0.5 + 1 / 16), n3 / 8
+    act = {"workload": f"activations [{T3} x {H3}] bf16, Student-t(4), 8 outlier channels x50; "
+                       "rollout and trainer copies alternate (268 MiB each)"}
+    act["amax"] = _bw_row("tq::amax_kernel<true>", _time_rotating(stream, amax, 2, reps), 2.0 * n3)
+    act["nearest_hint"] = _bw_row("tq::quantize_kernel<true, 1>",
+                                  _time_rotating(stream, nearest_hint, 2, reps), b_q + b_h,
+                                  note="tensor amax given")
+    act["guided"] = _bw_row("tq::quantize_kernel<true, 2>", _time_rotating(stream, guided, 2, reps),
+                            b_q + b_h, note="hints of the other copy, tensor amax given")
+    act["nearest_hint_from_scratch"] = _bw_row(
+        "tq::amax_kernel<true> + tq::quantize_kernel<true, 1>",
+        _time_rotating(stream, scratch_hint, 2, reps), b_q + b_h, b_q + b_h + 2.0 * n3,
+        note="tq_quantize without a given amax: fill, amax pass, quantize pass")
+    act["nearest_from_scratch"] = _bw_row(
+        "tq::amax_kernel<true> + tq::quantize_kernel<true, 0>",
+        _time_rotating(stream, scratch, 2, reps), b_q, b_q + 2.0 * n3,
+        note="tq_quantize without a given amax: fill, amax pass, quantize pass")
+    out["activations"] = act
+    del ar, at, X, h3, qa, qs
+
+    # ---- transpose-requantize 8192 x 8192, one call per seed, five source tensors ----
+    R4 = C4_ = 8192
+    n4 = R4 * C4_
+    srcs = []
+    for j in range(5):
+        src = inputs.transpose_source(R4, C4_, device=dev, seed=4 if j == 0 else 40 + j)
+        srcs.append((ops.quantize(src), ops.new_nvfp4((1,), C4_, R4, dev)))
+        del src
+
+    def sr(i):
+        q, qt = srcs[i % 5]
+        ok(L.tq_requant_transpose_sr(P(q.codes), P(q.scales), P(q.tensor_scale), 1, R4, C4_,
+                                     C.c_uint64(i), P(qt.codes), P(qt.scales), P(qt.tensor_scale),
+                                     sp), "SR transpose")
+    seeds = {"n": 0}
+
+    def sr_seeded(j):  # a new seed for every call
+        sr(j + 5 * seeds["n"])
+        seeds["n"] += j == 4
+    out["transpose_requant"] = {
+        "workload": f"NVFP4 [{R4} x {C4_}] (nearest-quantized N(0,1) bf16) -> transposed, "
+                    "stochastic-rounding requantize; a new Philox seed per call",
+        **_bw_row("tq::requant_transpose_sr_kernel<false>", _time_rotating(stream, sr_seeded, 5, reps),
+                  n4 * 2 * (0.5 + 1 / 16))}
+    del srcs
+
+    # ---- grouped GEMM: 32 experts, 16384 tokens, K 2048, N 768, three input sets ----
+    G5, T5, K5, N5 = 32, 16384, 2048, 768
+    sets = []
+    for j in range(3):
+        a5, w5, off5 = inputs.grouped_gemm_inputs(G5, T5, K5, N5, device=dev, seed=5 if j == 0 else 50 + j)
+        sets.append((a5, off5.to(dev), ops.quantize(w5), ops.quantize(a5.view(1, T5, K5)),
+                     torch.empty((T5, N5), dtype=torch.bfloat16, device=dev)))
+        del w5
+
+    def gemm(i):
+        a5, off5, q5, _, o5 = sets[i]
+        ok(L.tq_grouped_gemm_nvfp4(P(a5), P(off5), G5, T5, N5, K5, P(q5.codes), P(q5.scales),
+                                   P(q5.tensor_scale), P(o5), sp), "grouped GEMM")
+
+    def w4a4(i):
+        _, off5, q5, a5q, o5 = sets[i]
+        ok(L.tq_grouped_gemm_w4a4(P(a5q.codes), P(a5q.scales), P(a5q.tensor_scale), P(off5), G5, T5,
+                                  N5, K5, P(q5.codes), P(q5.scales), P(q5.tensor_scale), P(o5), sp),
+           "W4A4 grouped GEMM")
+    flops5 = 2.0 * T5 * K5 * N5
+    out["grouped_gemm"] = {
+        "workload": f"{G5} experts, Zipf(1.1) counts over {T5} tokens, K {K5}, N {N5}; "
+                    "A bf16 N(0,1), W NVFP4 from N(0,0.02)",
+        **_mfma_row("tq::grouped_gemm_nvfp4_kernel<false, true>", _time_rotating(stream, gemm, 3, reps),
+                    flops5)}
+    out["grouped_gemm_w4a4"] = {
+        "workload": "as grouped_gemm, activations NVFP4 (one tensor)",
+        **_mfma_row("tq::grouped_gemm_nvfp4_kernel<true, true>", _time_rotating(stream, w4a4, 3, reps),
+                    flops5)}
+    del sets
+    torch.cuda.synchronize()
+    return out
 
 
 def measure_extras(L, dev, stream, A, OFF, QG, QN, nl, first_hint):
@@ -337,8 +585,7 @@ def measure_extras(L, dev, stream, A, OFF, QG, QN, nl, first_hint):
     * 16x16-tile scaling: quantize and exact transpose of the activations
       workload [32768 x 4096] bf16, and the share of zero codes against block-16;
     * MXFP8 for the backward: nearest quantize of the activations workload and the
-      NVFP4 -> MXFP8 stochastic-rounding transpose of each layer's trainer weights;
-    * the grouped GEMM at 32 experts, 16384 tokens, K = 2048, N = 768."""
+      NVFP4 -> MXFP8 stochastic-rounding transpose of each layer's trainer weights."""
     import ctypes as C
 
     import torch
@@ -382,32 +629,6 @@ def measure_extras(L, dev, stream, A, OFF, QG, QN, nl, first_hint):
         "frac_bf16_mfma_peak": round(flops / us_g / 1e6 / BF16_MFMA_PEAK_TFLOPS, 4),
         "shape": f"{EXPERTS} experts, {TOKENS} tokens, K {COLS}, N {ROWS}"}
     del AQ, OUT
-
-    # ---- grouped GEMM at its own configuration: 32 experts, Zipf(1.1) token
-    # counts summing to 16384, K = 2048, N = 768; four input sets rotate so that
-    # the timed calls do not run from the 256 MB Infinity Cache ----
-    G5, T5, K5, N5 = 32, 16384, 2048, 768
-    sets5 = []
-    for i in range(4):
-        a5, w5, off5 = inputs.grouped_gemm_inputs(G5, T5, K5, N5, device=dev, seed=5 + i)
-        sets5.append((a5, ops.quantize(w5), off5.to(dev)))
-        del w5
-    out5 = torch.empty((T5, N5), dtype=torch.bfloat16, device=dev)
-
-    def gemm_c5():
-        for a5, q5, off5 in sets5:
-            st = L.tq_grouped_gemm_nvfp4(P(a5), P(off5), G5, T5, N5, K5, P(q5.codes), P(q5.scales),
-                                         P(q5.tensor_scale), P(out5), sp)
-            assert st == 0
-
-    us5 = _time_phase(stream, gemm_c5, 5) / len(sets5)
-    flops5 = 2.0 * T5 * K5 * N5
-    out["gemm_32_experts"] = {
-        "kernel": "tq::grouped_gemm_nvfp4_kernel", "avg_us": round(us5, 2),
-        "TFLOP/s": round(flops5 / us5 / 1e6, 1),
-        "frac_bf16_mfma_peak": round(flops5 / us5 / 1e6 / BF16_MFMA_PEAK_TFLOPS, 4),
-        "shape": f"{G5} experts, {T5} tokens, K {K5}, N {N5}, Zipf(1.1) counts"}
-    del sets5, out5
 
     # ---- FP4 KV cache with hints ----
     T, Hh, D = 32768, 8, 128
@@ -530,89 +751,266 @@ KERNEL_OF = {
     "quantize_hint": ("tq::quantize_kernel<true, 1>", "tq_quantize.hip"),
     "guided": ("tq::quantize_kernel<true, 2>", "tq_quantize.hip"),
     "mismatch": ("tq::mismatch_kernel", "tq_quantize.hip"),
-    "sr_transpose": ("tq::requant_transpose_sr_kernel", "tq_sr.hip"),
-    "gemm": ("tq::grouped_gemm_nvfp4_kernel", "tq_gemm.hip"),
+    "sr_transpose": ("tq::requant_transpose_sr_kernel<false>", "tq_sr.hip"),
+    "gemm": ("tq::grouped_gemm_nvfp4_kernel<false, true>", "tq_gemm.hip"),
 }
 
-# HBM bytes per layer covered, from rocprofv3 FETCH_SIZE and WRITE_SIZE passes
-# over this benchmark (KiB per dispatch scaled by what the same counters read for
-# the 1 GiB device copy of --copy-calibration, divided by the layers the
-# dispatch covers), keyed by the SHA-256 of the kernel's source and the shared
-# device header: a figure is reported only for the code it was measured on.
-TRAFFIC = {
-    # FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0: the 1 GiB copy read 524314 KiB fetched and
-    # 1048576 KiB written.  Ratio to the algorithmic bytes in the comments.
-    "amax": {"bytes_per_layer": 201325797, "fetch_kib": 4718757.1, "write_kib": 96.0, "layers": 48, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.000
-    "quantize": {"bytes_per_layer": 257944055, "fetch_kib": 3538979.9, "write_kib": 1990733.5, "layers": 36, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.000
-    "quantize_hint": {"bytes_per_layer": 270528010, "fetch_kib": 2359332.4, "write_kib": 1622067.1, "layers": 24, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.000
-    "guided": {"bytes_per_layer": 270530639, "fetch_kib": 2506847.8, "write_kib": 1327112.6, "layers": 24, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.000
-    "mismatch": {"bytes_per_layer": 101033841, "fetch_kib": 1769513.6, "write_kib": 13117.7, "layers": 36, "sources_sha256": "219cc3dce9ba5a108375d338a1ab9131292a3111e54af0e89ed55b8b9ad46fdd"},  # 1.004
-    "sr_transpose": {"bytes_per_layer": 135414149, "fetch_kib": 674280.6, "write_kib": 1825274.2, "layers": 24, "sources_sha256": "eac8271f5410576433458a8d725da328e8b742bdd99a233b77055ff5c6fc8f42"},  # 1.196
-    "gemm": {"bytes_per_layer": 159250907, "fetch_kib": 44993.4, "write_kib": 65536.0, "layers": 1, "sources_sha256": "234bcd5a07abdf64d459419c0990277f1f94565dcccbe9d323ff0f877f428939"},  # 1.070
-}
+# HBM-side traffic.  Two rocprofv3 --pmc passes over this benchmark count the L2's
+# requests to the memory fabric per dispatch: TCC_EA0_RDREQ (of which
+# TCC_EA0_RDREQ_32B are 32-byte reads; the rest are 128-byte reads on this GPU)
+# and TCC_EA0_WRREQ (of which TCC_EA0_WRREQ_64B are 64-byte writes; the rest 32-byte).
+# `--traffic-from DIR... --traffic-section step|configs` turns the counter CSVs into
+# profiles/hbm_traffic.json, keyed by the SHA-256 of the library's sources, so a
+# figure is reported only for the code it was measured on.
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+# layers each step kernel covers per step (48 layers, hints for the latter 24)
+STEP_LAYERS = {"amax": 96, "quantize": 72, "quantize_hint": 24, "guided": 24, "mismatch": 72,
+               "sr_transpose": 48, "gemm": 48}
 
 
-def _sources_digest(src):
+def _sources_digest():
     import hashlib
     h = hashlib.sha256()
-    for f in (src, "tq_device.hpp"):
-        with open(os.path.join(ROOT, "fp4_quantization_precision_amd", "csrc", f), "rb") as fh:
+    d = os.path.join(ROOT, "fp4_quantization_precision_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        h.update(f.encode())
+        with open(os.path.join(d, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
 
+def _short_kernel(name):
+    import re
+    name = name.replace("void ", "", 1)
+    m = re.match(r"([\w:]+(<[^()]*>)?)", name)
+    return m.group(1) if m else name
+
+
+def traffic_from(dirs, section):
+    """Per-kernel HBM bytes from rocprofv3 counter CSVs (one --pmc pass with the read
+    request counters, one with the write request counters) into TRAFFIC_JSON."""
+    import csv
+    import glob
+    per = {}  # kernel -> {counter: {dispatch: value}}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    k = _short_kernel(r["Kernel_Name"])
+                    c = r["Counter_Name"].replace("_sum", "")
+                    per.setdefault(k, {}).setdefault(c, {})[r["Dispatch_Id"]] = float(r["Counter_Value"])
+    kernels = {}
+    for k, cs in per.items():
+        need = ("TCC_EA0_RDREQ", "TCC_EA0_RDREQ_32B", "TCC_EA0_WRREQ", "TCC_EA0_WRREQ_64B")
+        if not all(c in cs for c in need):
+            continue
+        tot = {c: sum(cs[c].values()) for c in need}
+        n = len(cs["TCC_EA0_RDREQ"])
+        rd = 128 * (tot["TCC_EA0_RDREQ"] - tot["TCC_EA0_RDREQ_32B"]) + 32 * tot["TCC_EA0_RDREQ_32B"]
+        wr = 64 * tot["TCC_EA0_WRREQ_64B"] + 32 * (tot["TCC_EA0_WRREQ"] - tot["TCC_EA0_WRREQ_64B"])
+        ent = {"dispatches": n, "read_bytes_per_dispatch": round(rd / n),
+               "write_bytes_per_dispatch": round(wr / n), "bytes_per_dispatch": round((rd + wr) / n),
+               "counters_per_dispatch": {c: round(v / n, 1) for c, v in tot.items()}}
+        kernels[k] = ent
+    if section == "step":
+        for cat, (kname, _) in KERNEL_OF.items():
+            if kname in kernels:
+                e = kernels[kname]
+                e["bytes_per_layer"] = round(e["bytes_per_dispatch"] * e["dispatches"] / STEP_LAYERS[cat])
+    data = {}
+    if os.path.exists(TRAFFIC_JSON):
+        with open(TRAFFIC_JSON) as fh:
+            data = json.load(fh)
+    data[section] = {"sources_sha256": _sources_digest(), "kernels": kernels}
+    data["method"] = ("bytes = 128 x (TCC_EA0_RDREQ - TCC_EA0_RDREQ_32B) + 32 x TCC_EA0_RDREQ_32B "
+                      "+ 64 x TCC_EA0_WRREQ_64B + 32 x (TCC_EA0_WRREQ - TCC_EA0_WRREQ_64B), "
+                      "summed over the XCDs' L2 channels, averaged per dispatch")
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    return data
+
+
+def _traffic_entry(section, kname):
+    if not os.path.exists(TRAFFIC_JSON):
+        return None
+    with open(TRAFFIC_JSON) as fh:
+        sec = json.load(fh).get(section)
+    if not sec or sec.get("sources_sha256") != _sources_digest():
+        return None
+    return sec["kernels"].get(kname)
+
+
 def measured_traffic(cat, layers_per_launch):
-    """Counter-measured HBM bytes per launch of `cat`, or None if not measured on
-    the current sources."""
-    ent = TRAFFIC.get(cat)
-    if ent is None or _sources_digest(KERNEL_OF[cat][1]) != ent["sources_sha256"]:
+    """Counter-measured HBM bytes per launch of a step kernel, or None if not measured
+    on the current sources."""
+    ent = _traffic_entry("step", KERNEL_OF[cat][0])
+    if ent is None or "bytes_per_layer" not in ent:
         return None
     return round(ent["bytes_per_layer"] * layers_per_launch)
 
 
+def _cpu_threads():
+    """Host threads for the threaded oracle runs: every core this process may use,
+    at most 16 (the host share of one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def _run_units(unit, n_units, threads):
+    """Wall time of unit(0..n_units-1) on `threads` host threads (the oracle's C
+    calls release the GIL, so the threads run in parallel)."""
+    from concurrent.futures import ThreadPoolExecutor
+    t0 = time.perf_counter()
+    if threads == 1:
+        for i in range(n_units):
+            unit(i)
+    else:
+        with ThreadPoolExecutor(max_workers=threads) as ex:
+            list(ex.map(unit, range(n_units)))
+    return time.perf_counter() - t0
+
+
 def cpu_baseline(XR, XT, A, counts, first_hint):
-    """The CPU oracle on a bounded sample of one step: experts 0 and 1 of layer
-    `first_hint` (a hinted layer) through amax, nearest (rollout + trainer),
-    hints, guided, mismatch counts and the SR transpose, plus the grouped-GEMM
-    rows of the same share of the layer's tokens (2/64 of 16384 rows), scaled to
-    GB/s with the same algorithmic bytes as the GPU step."""
+    """The CPU oracle as it stands, timed on the host on bounded samples of each
+    workload, once on one thread and once on every usable core (one sample unit per
+    thread; the oracle's C routines release the GIL).  Rates use the same
+    algorithmic bytes (or flops) as the GPU rows.
+
+    * step: per unit, one expert of layer `first_hint` (a hinted layer) through
+      amax (both copies), nearest + hint, nearest, guided, two mismatch counts and
+      the SR transpose, plus that expert's share of the layer's grouped GEMM (256 of
+      16384 token rows, fp64);
+    * activations: per unit, 1024 rows x 4096: amax, nearest + hint, guided;
+    * transpose-requantize: per unit, a 1024-row slab of the 8192^2 NVFP4 tensor;
+    * grouped GEMM 32 experts, K 2048, N 768: per unit, 64 token rows in fp64."""
     import numpy as np
+    import torch
 
     import oracle
-    l, ne = first_hint, 2
-    per = ROWS * COLS
-    xr = XR[l, :ne].cpu()
-    xt = XT[l, :ne].cpu()
-    a = A[l].cpu()
+    from fp4_quantization_precision_amd import inputs
+
+    T = _cpu_threads()
+    res = {}
+
+    def rates(name, unit, unit_bytes=None, unit_flops=None, what=""):
+        t1 = _run_units(unit, 1, 1)
+        tT = _run_units(unit, T, T)
+        r = {"sample_unit": what, "units_all_cores": T, "seconds_1core": round(t1, 3),
+             "seconds_all_cores": round(tT, 3)}
+        if unit_bytes is not None:
+            r["GB/s_1core"] = round(unit_bytes / t1 / 1e9, 5)
+            r["GB/s_all_cores"] = round(T * unit_bytes / tT / 1e9, 5)
+        if unit_flops is not None:
+            r["GFLOP/s_1core"] = round(unit_flops / t1 / 1e9, 4)
+            r["GFLOP/s_all_cores"] = round(T * unit_flops / tT / 1e9, 4)
+        res[name] = r
+        return r
+
+    # ---- step sample (MoE weights, one hinted layer) ----
+    l, per = first_hint, ROWS * COLS
+    xr_l = XR[l].cpu()
+    xt_l = XT[l].cpu()
+    a_l = A[l].cpu()
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
-    rows = np.arange(0, TOKENS, 16)[: 2 * TOKENS * ne // EXPERTS]  # 1024 token rows spread over the layer
-    t0 = time.perf_counter()
-    qr = oracle.quantize(xr, ne, ROWS, COLS)
-    h = oracle.extract_hint(qr["codes"], ne * per)
-    qn = oracle.quantize(xt, ne, ROWS, COLS)
-    qg = oracle.quantize_guided(xt, ne, ROWS, COLS, h, amax=qn["tensor_amax"])
-    oracle.code_mismatch(qr["codes"], qn["codes"], ne, per)
-    oracle.code_mismatch(qr["codes"], qg["codes"], ne, per)
-    oracle.requant_transpose_sr(qg["codes"], qg["scales"], qg["tensor_scale"], ne, ROWS, COLS, l)
-    t_q = time.perf_counter() - t0
-    # GEMM rows need every expert's weights: quantize the trainer weights of all
-    # experts with the GPU-independent oracle first (not timed: it is the
-    # quantize step, already sampled above), then time the rows.
-    wq = oracle.quantize(XT[l].cpu(), EXPERTS, ROWS, COLS)
-    t1 = time.perf_counter()
-    oracle.grouped_gemm(a, off, ROWS, COLS, wq["codes"], wq["scales"], wq["tensor_scale"], rows=rows)
-    t_g = time.perf_counter() - t1
-    n = ne * per
-    q_bytes = n * (2.0 * 2 + (2 + 0.5 + 1 / 16 + 1 / 8) + (2 + 0.5 + 1 / 16) + (2 + 1 / 8 + 0.5 + 1 / 16)
-                   + 2 * 1.0 + 2 * (0.5 + 1 / 16))
-    g_bytes = (TOKENS * COLS * 2 + EXPERTS * per * (0.5 + 1 / 16) + TOKENS * ROWS * 2) * rows.size / TOKENS
-    secs = t_q + t_g
-    return {"value": round((q_bytes + g_bytes) / secs / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"layer {l}, experts 0-1 ({n} weights): amax, nearest x2, hints, guided, "
-                      f"mismatch x2, SR transpose ({t_q:.1f} s); grouped-GEMM fp64 rows "
-                      f"{rows.size}/{TOKENS} of the layer ({t_g:.1f} s)",
-            "seconds": round(secs, 2)}
+    # untimed: the layer's trainer weights in the oracle's own encoding for the GEMM rows
+    wq_parts = [None] * EXPERTS
+
+    def prep(e):
+        wq_parts[e] = oracle.quantize(xt_l[e], 1, ROWS, COLS)
+    _run_units(prep, EXPERTS, T)
+    wq = {"codes": np.concatenate([q["codes"] for q in wq_parts]),
+          "scales": np.concatenate([q["scales"] for q in wq_parts]),
+          "tensor_scale": np.concatenate([q["tensor_scale"] for q in wq_parts])}
+    del wq_parts
+
+    def step_unit(i):
+        e = i % EXPERTS
+        xr, xt = xr_l[e], xt_l[e]
+        oracle.tensor_amax(xr, 1, per)
+        am = oracle.tensor_amax(xt, 1, per)
+        qr = oracle.quantize(xr, 1, ROWS, COLS)
+        h = oracle.extract_hint(qr["codes"], per)
+        qn = oracle.quantize(xt, 1, ROWS, COLS, amax=am)
+        qg = oracle.quantize_guided(xt, 1, ROWS, COLS, h, amax=am)
+        oracle.code_mismatch(qr["codes"], qn["codes"], 1, per)
+        oracle.code_mismatch(qr["codes"], qg["codes"], 1, per)
+        oracle.requant_transpose_sr(qg["codes"], qg["scales"], qg["tensor_scale"], 1, ROWS, COLS, 1)
+        rows = np.arange(e, TOKENS, EXPERTS)  # 256 rows spread over the layer
+        oracle.grouped_gemm(a_l, off, ROWS, COLS, wq["codes"], wq["scales"], wq["tensor_scale"],
+                            rows=rows)
+    chain_b = per * (2.0 * 2 + (2 + 0.5 + 1 / 16 + 1 / 8) + (2 + 0.5 + 1 / 16) +
+                     (2 + 1 / 8 + 0.5 + 1 / 16) + 2 * 1.0 + 2 * (0.5 + 1 / 16))
+    gemm_b = (TOKENS * COLS * 2 + EXPERTS * per * (0.5 + 1 / 16) + TOKENS * ROWS * 2) / EXPERTS
+    step = rates("step", step_unit, unit_bytes=chain_b + gemm_b,
+                 what=f"one expert of layer {l} ({per} weights) through the step's quantizer chain "
+                      f"and SR transpose, plus {TOKENS // EXPERTS} fp64 grouped-GEMM rows")
+    del xr_l, xt_l, a_l, wq
+
+    # ---- activations ----
+    T3, H3, R3 = 32768, 4096, 1024
+    ar, at, _ = inputs.activations(T3, H3, device=XR.device)
+    ar_h, at_h = ar.cpu(), at.cpu()
+    del ar, at
+    # the whole tensor's maxima, given to the sampled rows (untimed)
+    am_r = float(oracle.tensor_amax(ar_h, 1, T3 * H3)[0])
+    am_t = float(oracle.tensor_amax(at_h, 1, T3 * H3)[0])
+    ar_c, at_c = ar_h[: R3 * T], at_h[: R3 * T]
+    del ar_h, at_h
+
+    def act_unit(i):
+        xr, xt = ar_c[i * R3:(i + 1) * R3], at_c[i * R3:(i + 1) * R3]
+        oracle.tensor_amax(xr, 1, R3 * H3)
+        q = oracle.quantize(xr, 1, R3, H3, amax=[am_r])
+        h = oracle.extract_hint(q["codes"], R3 * H3)
+        oracle.quantize_guided(xt, 1, R3, H3, h, amax=[am_t])
+    rates("activations", act_unit, unit_bytes=R3 * H3 * (2 + 2 * (2.5625 + 0.125)),
+          what=f"{R3} rows x {H3}: amax, nearest + hint, guided")
+    del ar_c, at_c
+
+    # ---- transpose-requantize slabs of the 8192^2 tensor ----
+    R4, C4_ = 1024, 8192
+    n_slabs = min(T, 8192 // R4)  # more threads than slabs reuse them
+    src = inputs.transpose_source(8192, 8192, device=XR.device)[: R4 * n_slabs].cpu()
+    slabs = [None] * n_slabs
+
+    def prep4(i):
+        slabs[i] = oracle.quantize(src[i * R4:(i + 1) * R4], 1, R4, C4_)
+    _run_units(prep4, n_slabs, T)
+
+    def sr_unit(i):
+        q = slabs[i % n_slabs]
+        oracle.requant_transpose_sr(q["codes"], q["scales"], q["tensor_scale"], 1, R4, C4_, i)
+    rates("transpose_requant", sr_unit, unit_bytes=R4 * C4_ * 2 * (0.5 + 1 / 16),
+          what=f"a {R4} x {C4_} slab of the nearest-quantized 8192^2 tensor")
+    del src, slabs
+
+    # ---- grouped GEMM rows, 32 experts ----
+    G5, T5, K5, N5, R5 = 32, 16384, 2048, 768, 64
+    a5, w5, off5 = inputs.grouped_gemm_inputs(G5, T5, K5, N5, device=XR.device, seed=5)
+    a5, w5 = a5.cpu(), w5.cpu()
+    parts = [None] * G5
+
+    def prep5(e):
+        parts[e] = oracle.quantize(w5[e], 1, N5, K5)
+    _run_units(prep5, G5, T)
+    w5q = {k: np.concatenate([q[k] for q in parts]) for k in ("codes", "scales", "tensor_scale")}
+    del parts, w5
+
+    def gemm_unit(i):
+        rows = np.arange(i, T5, T5 // R5)[:R5]
+        oracle.grouped_gemm(a5, off5, N5, K5, w5q["codes"], w5q["scales"], w5q["tensor_scale"],
+                            rows=rows)
+    rates("grouped_gemm", gemm_unit, unit_flops=2.0 * R5 * K5 * N5,
+          what=f"{R5} token rows spread over the {G5} experts, fp64")
+
+    return {"value": step["GB/s_all_cores"], "unit": "GB/s", "cores": T, "kind": "oracle",
+            "sample": f"per thread: {step['sample_unit']}; {T} threads, "
+                      f"{step['seconds_all_cores']} s",
+            "value_1core": step["GB/s_1core"], "per_config": res}
 
 
 if __name__ == "__main__":

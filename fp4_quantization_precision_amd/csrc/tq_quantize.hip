@@ -23,32 +23,11 @@ constexpr int kThreads = 256;
 // kernels that also write (quantize, mismatch) run fastest with one work item
 // per lane and no grid-stride reuse: consecutive workgroups then cover
 // consecutive memory (measured on MI355X: 5.3 -> 5.8 TB/s for the nearest
-// quantizer between 128k workgroups and one block per lane).
-#ifndef TQ_AMAX_GROUPS
-#define TQ_AMAX_GROUPS 1024
-#endif
-#ifndef TQ_STREAM_NT
-#define TQ_STREAM_NT 0
-#endif
-#ifndef TQ_AMAX_UNROLL
-#define TQ_AMAX_UNROLL 4
-#endif
-constexpr int kAmaxUnroll = TQ_AMAX_UNROLL;
-
-// 16-byte load of data read exactly once (nontemporal: no reuse expected in cache)
-__device__ __forceinline__ uint4 stream_load16(const uint4* p)
-{
-#if TQ_STREAM_NT
-    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-    const u32x4v v = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(p));
-    return make_uint4(v[0], v[1], v[2], v[3]);
-#else
-    return *p;
-#endif
-}
-#ifndef TQ_QUANT_GROUPS
-#define TQ_QUANT_GROUPS (1 << 30)  // i.e. as many as there are work items
-#endif
+// quantizer between 128k workgroups and one block per lane).  Nontemporal
+// loads for the read-once streams were measured and not kept.
+constexpr int64_t kAmaxGroups = 1024;
+constexpr int kAmaxUnroll = 4;
+constexpr int64_t kQuantGroups = (int64_t)1 << 30;  // as many as there are work items
 
 // ---------------------------------------------------------------------------
 // small fills (used instead of memset nodes, which misbehave under graph replay)
@@ -122,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict_
             uint4 q[kAmaxUnroll];
 #pragma unroll
             for (int u = 0; u < kAmaxUnroll; ++u)
-                q[u] = stream_load16(xb + i + u * stride);
+                q[u] = xb[i + u * stride];
 #pragma unroll
             for (int u = 0; u < kAmaxUnroll; ++u)
                 m = abs_bits_max(q[u], BF16, m);
@@ -166,7 +145,7 @@ void launch_amax(const void* x, bool bf16, int64_t batch, int64_t per_tensor, fl
     const int64_t vec = per_tensor * (bf16 ? 2 : 4) / 16;
     if (vec == 0)
         return;
-    dim3 grid(groups_per_tensor(vec, batch, TQ_AMAX_GROUPS), grid_y(batch));
+    dim3 grid(groups_per_tensor(vec, batch, kAmaxGroups), grid_y(batch));
     if (bf16)
         hipLaunchKernelGGL(amax_kernel<true>, grid, dim3(kThreads), 0, s,
                            static_cast<const uint4*>(x), vec, batch, amax);
@@ -285,7 +264,7 @@ void launch_quantize(const void* x, bool bf16, int64_t batch, int64_t rows, int6
 {
     const int64_t bpt = rows * cols / 16;
     const int64_t total = bpt * batch;
-    dim3 grid(groups_per_tensor(bpt, batch, TQ_QUANT_GROUPS), grid_y(batch));
+    dim3 grid(groups_per_tensor(bpt, batch, kQuantGroups), grid_y(batch));
     uint2* c2 = reinterpret_cast<uint2*>(codes);
     uint16_t* h = reinterpret_cast<uint16_t*>(hints);
 #define TQ_QLAUNCH(B, M)                                                                     \
@@ -417,7 +396,7 @@ void launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float*
                        int64_t rows, int64_t cols, float* out, hipStream_t s)
 {
     const int64_t bpt = rows * cols / 16;
-    dim3 grid(groups_per_tensor(bpt, batch, TQ_QUANT_GROUPS), grid_y(batch));
+    dim3 grid(groups_per_tensor(bpt, batch, kQuantGroups), grid_y(batch));
     hipLaunchKernelGGL(dequantize_kernel, grid, dim3(kThreads), 0, s,
                        reinterpret_cast<const uint2*>(codes), scales, ts, bpt, batch,
                        reinterpret_cast<float4*>(out));
@@ -502,7 +481,7 @@ void launch_mismatch(const uint8_t* a, const uint8_t* b, int64_t batch, int64_t 
     const int64_t vec = per_tensor / 32;
     if (vec == 0)
         return;
-    dim3 grid(groups_per_tensor(vec, batch, TQ_QUANT_GROUPS), grid_y(batch));
+    dim3 grid(groups_per_tensor(vec, batch, kQuantGroups), grid_y(batch));
     hipLaunchKernelGGL(mismatch_kernel, grid, dim3(kThreads), 0, s,
                        reinterpret_cast<const uint4*>(a), reinterpret_cast<const uint4*>(b), vec,
                        batch, reinterpret_cast<unsigned long long*>(counts));

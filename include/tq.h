@@ -84,7 +84,12 @@ enum { TQ_F32 = 0, TQ_BF16 = 1 };
 enum { TQ_AMAX_GIVEN = 1u << 0 };
 
 /*
- * tq_tensor_amax - per-tensor maximum of |x|.
+ * tq_tensor_amax - per-tensor maximum of |x|: the first step of the two-level scale.
+ * [RLQ] "RL에서 양자화를 사용하는 방법", the paragraph on the shared convention of
+ * Fig. 2: both engines must agree not only on the codes but on the scale that
+ * turns a stored code into a value.  Here that scale is the product of the E4M3
+ * block scale and a per-tensor fp32 scale s_t = A_T / 2688 (2688 = 6 * 448, the
+ * largest E2M1 magnitude times the largest E4M3 value), and A_T is this maximum.
  *   x          [batch][per_tensor] fp32 or bf16, 16-byte aligned.
  *   amax       [batch] fp32 output; amax[t] = max_i |x[t][i]| (0 for empty tensors).
  * per_tensor must be a multiple of 16.  Inputs must be finite.

@@ -279,6 +279,30 @@ def test_quantize_all_zero_and_empty_tensors(orc):
     assert (q["tensor_scale"] == 0).all() and (q["tensor_amax"] == 0).all()
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_tensor_amax_matches_numpy(orc, dtype):
+    """The oracle's per-tensor amax against numpy's max |x| per tensor of a batch:
+    random tensors of mixed magnitudes, a tensor whose maximum is negative, one of
+    subnormals only, one of signed zeros, and single-block tensors."""
+    rng = np.random.default_rng(21)
+    shapes = [(7, 48), (3, 4096), (1, 16), (5, 16 * 65)]
+    for batch, per in shapes:
+        x = (rng.standard_normal((batch, per)) *
+             np.exp2(rng.uniform(-40, 40, (batch, 1)))).astype(np.float32)
+        x[0] = -np.abs(x[0])                                       # maximum |x| at a negative value
+        if batch > 2:
+            x[1] = (rng.standard_normal(per) * 1e-39).astype(np.float32)  # subnormals only
+            x[2] = np.where(rng.random(per) < 0.5, -0.0, 0.0).astype(np.float32)
+        if dtype == "bf16":
+            t = torch.from_numpy(x).to(torch.bfloat16)
+            want = t.float().abs().amax(dim=1).numpy()
+            got = orc.tensor_amax(t.view(torch.int16).numpy().view(np.uint16), batch, per)
+        else:
+            want = np.abs(x).max(axis=1)
+            got = orc.tensor_amax(x, batch, per)
+        assert np.array_equal(got, want.astype(np.float32)), (batch, per)
+
+
 def test_quantize_amax_given_matches_computed(orc):
     x = _random_tensor("outliers", 3, 16, 128, 9)
     q1 = orc.quantize(x, 3, 16, 128)
