@@ -355,6 +355,20 @@ def measure_step(args, L, dev, stream):
             "cpu_args": (XR, XT, A, counts, first_hint)}
 
 
+def _time_phase(stream, fn, reps):
+    """Average event time (us) of `reps` back-to-back calls of fn on `stream`."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return 1e3 * e0.elapsed_time(e1) / reps
+
+
 def _time_rotating(stream, call, n_sets, reps):
     """Average event time (us) per call of `reps` back-to-back calls call(i), where
     call i works on buffer set i % n_sets; the sets together exceed the 256 MiB
@@ -499,18 +513,18 @@ def measure_configs(L, dev, stream, reps):
     b_q, b_h = n3 * (2 + 0.5 + 1 / 16), n3 / 8
     act = {"workload": f"activations [{T3} x {H3}] bf16, Student-t(4), 8 outlier channels x50; "
                        "rollout and trainer copies alternate (268 MiB each)"}
-    act["amax"] = _bw_row("tq::amax_kernel<true>", _time_rotating(stream, amax, 2, reps), 2.0 * n3)
+    act["amax"] = _bw_row("tq::amax_kernel<true, 1024>", _time_rotating(stream, amax, 2, reps), 2.0 * n3)
     act["nearest_hint"] = _bw_row("tq::quantize_kernel<true, 1>",
                                   _time_rotating(stream, nearest_hint, 2, reps), b_q + b_h,
                                   note="tensor amax given")
     act["guided"] = _bw_row("tq::quantize_kernel<true, 2>", _time_rotating(stream, guided, 2, reps),
                             b_q + b_h, note="hints of the other copy, tensor amax given")
     act["nearest_hint_from_scratch"] = _bw_row(
-        "tq::amax_kernel<true> + tq::quantize_kernel<true, 1>",
+        "tq::amax_kernel<true, 1024> + tq::quantize_kernel<true, 1>",
         _time_rotating(stream, scratch_hint, 2, reps), b_q + b_h, b_q + b_h + 2.0 * n3,
         note="tq_quantize without a given amax: fill, amax pass, quantize pass")
     act["nearest_from_scratch"] = _bw_row(
-        "tq::amax_kernel<true> + tq::quantize_kernel<true, 0>",
+        "tq::amax_kernel<true, 1024> + tq::quantize_kernel<true, 0>",
         _time_rotating(stream, scratch, 2, reps), b_q, b_q + 2.0 * n3,
         note="tq_quantize without a given amax: fill, amax pass, quantize pass")
     out["activations"] = act
@@ -620,9 +634,12 @@ def measure_extras(L, dev, stream, A, OFF, QG, QN, nl, first_hint):
     flops = 2.0 * TOKENS * COLS * ROWS
     n_a = TOKENS * COLS
     out["w4a4_quantize_activations"] = {
-        "kernel": "tq::amax_kernel + tq::quantize_kernel (tq_quantize, batch 1)",
-        "avg_us": round(us_q, 2), "GB/s": round(n_a * (2 + 2 + 0.5625) / us_q / 1e3, 1),
-        "note": "amax pass + quantize pass over [16384 x 768] bf16 per layer"}
+        "kernel": "tq::amax_kernel<true, 1024> + tq::quantize_kernel<true, 0> (tq_quantize from scratch)",
+        "avg_us": round(us_q, 2), "GB/s": round(n_a * (2 + 0.5625) / us_q / 1e3, 1),
+        "frac_hbm_peak": round(n_a * (2 + 0.5625) / us_q / 1e3 / HBM_PEAK_GBS, 4),
+        "GB/s_moved": round(n_a * (4 + 0.5625) / us_q / 1e3, 1),
+        "note": "[16384 x 768] bf16 per layer, tensor amax not given: fill, amax pass, quantize "
+                "pass; GB/s counts each byte once, GB/s_moved counts the input twice"}
     out["w4a4_gemm"] = {
         "kernel": "tq::grouped_gemm_nvfp4_kernel<true>", "avg_us": round(us_g, 2),
         "TFLOP/s": round(flops / us_g / 1e6, 1),
@@ -656,9 +673,12 @@ def measure_extras(L, dev, stream, A, OFF, QG, QN, nl, first_hint):
     us_h = _time_phase(stream, kv_hint, 5) / 2
     us_gd = _time_phase(stream, kv_guided, 5) / 2
     out["kv_quantize_hint"] = {
-        "kernel": "tq::amax_kernel + tq::quantize_kernel<true, 1>", "avg_us": round(us_h, 2),
-        "GB/s": round(n * (2 + 2 + 0.6875) / us_h / 1e3, 1),
-        "note": "per K or V tensor [32768 x 8 x 128]: amax pass + quantize with hints"}
+        "kernel": "tq::amax_kernel<true, 1024> + tq::quantize_kernel<true, 1>", "avg_us": round(us_h, 2),
+        "GB/s": round(n * (2 + 0.6875) / us_h / 1e3, 1),
+        "frac_hbm_peak": round(n * (2 + 0.6875) / us_h / 1e3 / HBM_PEAK_GBS, 4),
+        "GB/s_moved": round(n * (4 + 0.6875) / us_h / 1e3, 1),
+        "note": "per K or V tensor [32768 x 8 x 128], tensor amax not given: fill, amax pass, "
+                "nearest + hints pass; GB/s counts each byte once, GB/s_moved counts the input twice"}
     out["kv_guided"] = {
         "kernel": "tq::quantize_kernel<true, 2>", "avg_us": round(us_gd, 2),
         "GB/s": round(n * 2.6875 / us_gd / 1e3, 1),
@@ -746,7 +766,7 @@ def measure_extras(L, dev, stream, A, OFF, QG, QN, nl, first_hint):
 
 # kernel name and source file of each timed category
 KERNEL_OF = {
-    "amax": ("tq::amax_kernel<true>", "tq_quantize.hip"),
+    "amax": ("tq::amax_kernel<true, 256>", "tq_quantize.hip"),
     "quantize": ("tq::quantize_kernel<true, 0>", "tq_quantize.hip"),
     "quantize_hint": ("tq::quantize_kernel<true, 1>", "tq_quantize.hip"),
     "guided": ("tq::quantize_kernel<true, 2>", "tq_quantize.hip"),

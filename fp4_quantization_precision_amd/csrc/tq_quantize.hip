@@ -17,15 +17,27 @@ namespace tq {
 
 constexpr int kThreads = 256;
 
-// Workgroups per launch of the streaming kernels (spread over the batch).  The
-// read-only amax stream (unrolled, several 16-byte loads in flight per lane)
-// reaches its best HBM rate with about a thousand grid-stride workgroups.  The
-// kernels that also write (quantize, mismatch) run fastest with one work item
-// per lane and no grid-stride reuse: consecutive workgroups then cover
-// consecutive memory (measured on MI355X: 5.3 -> 5.8 TB/s for the nearest
-// quantizer between 128k workgroups and one block per lane).  Nontemporal
-// loads for the read-once streams were measured and not kept.
-constexpr int64_t kAmaxGroups = 1024;
+// Workgroups per launch of the streaming kernels (spread over the batch).
+//
+// The amax stream is read-only, with several 16-byte loads in flight per lane in a
+// grid-stride loop, and each workgroup publishes its maximum with one device-scope
+// atomic.  Such atomics on one address are serialised on MI355X (about 12 ns each,
+// measured), so the number of workgroups per tensor matters:
+//  - A launch of many tensors (at least one per CU) uses 256-thread workgroups,
+//    about a thousand in all.  Their atomics go to different addresses.
+//  - Fewer tensors use 1024-thread workgroups, about one per CU in all.  For one
+//    tensor this measured 5.69 TB/s against 5.08 TB/s with 1024 workgroups of 256
+//    (268 MB); for 25 MB it took 10.1 us against 18.7 us.
+//
+// The kernels that also write (quantize, mismatch) run fastest with one work item
+// per lane and no grid-stride reuse, because consecutive workgroups then cover
+// consecutive memory (measured on MI355X: 5.3 -> 5.8 TB/s for the nearest quantizer
+// between 128k workgroups and one block per lane).  Nontemporal loads for the
+// read-once streams were measured and not kept.
+constexpr int64_t kAmaxGroups = 1024;      // 256-thread workgroups, many tensors
+constexpr int64_t kAmaxWideGroups = 256;   // 1024-thread workgroups, fewer tensors
+constexpr int64_t kAmaxWideBelowBatch = 256;
+constexpr int kAmaxWideThreads = 1024;
 constexpr int kAmaxUnroll = 4;
 constexpr int64_t kQuantGroups = (int64_t)1 << 30;  // as many as there are work items
 
@@ -85,17 +97,16 @@ __device__ __forceinline__ uint32_t abs_bits_max(uint4 q, bool bf16, uint32_t m)
 
 // |x| of finite binary32 values orders like the unsigned integer of its bits,
 // so the maximum is taken on bit patterns and published with an integer atomic.
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict__ x,
-                                                        int64_t vec_per_tensor, int64_t batch,
-                                                        float* __restrict__ amax)
+template <bool BF16, int T>
+__global__ __launch_bounds__(T) void amax_kernel(const uint4* __restrict__ x, int64_t vec_per_tensor,
+                                                 int64_t batch, float* __restrict__ amax)
 {
-    __shared__ uint32_t red[kThreads / 64];
+    __shared__ uint32_t red[T / 64];
     for (int64_t b = blockIdx.y; b < batch; b += gridDim.y) {
         const uint4* xb = x + b * vec_per_tensor;
         uint32_t m = 0;
-        const int64_t stride = (int64_t)gridDim.x * kThreads;
-        int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+        const int64_t stride = (int64_t)gridDim.x * T;
+        int64_t i = (int64_t)blockIdx.x * T + threadIdx.x;
         // kAmaxUnroll independent 16-byte loads in flight per lane
         for (; i + (kAmaxUnroll - 1) * stride < vec_per_tensor; i += kAmaxUnroll * stride) {
             uint4 q[kAmaxUnroll];
@@ -116,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict_
         if (threadIdx.x == 0) {
             uint32_t r = red[0];
 #pragma unroll
-            for (int w = 1; w < kThreads / 64; ++w)
+            for (int w = 1; w < T / 64; ++w)
                 r = r > red[w] ? r : red[w];
             if (r != 0)
                 atomicMax(reinterpret_cast<unsigned int*>(amax + b), r);
@@ -127,10 +138,12 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const uint4* __restrict_
 
 static unsigned grid_y(int64_t batch) { return (unsigned)(batch < 65535 ? batch : 65535); }
 
-// Workgroups per tensor so that the whole launch has about `target` groups.
-static unsigned groups_per_tensor(int64_t work_items, int64_t batch, int64_t target)
+// Workgroups per tensor so that the whole launch has about `target` groups of
+// `threads` lanes.
+static unsigned groups_per_tensor(int64_t work_items, int64_t batch, int64_t target,
+                                  int64_t threads = kThreads)
 {
-    int64_t need = (work_items + kThreads - 1) / kThreads;
+    int64_t need = (work_items + threads - 1) / threads;
     int64_t cap = target / (batch < 1 ? 1 : batch);
     if (cap < 1)
         cap = 1;
@@ -145,13 +158,22 @@ void launch_amax(const void* x, bool bf16, int64_t batch, int64_t per_tensor, fl
     const int64_t vec = per_tensor * (bf16 ? 2 : 4) / 16;
     if (vec == 0)
         return;
+    const uint4* xv = static_cast<const uint4*>(x);
+    if (batch < kAmaxWideBelowBatch) {
+        dim3 grid(groups_per_tensor(vec, batch, kAmaxWideGroups, kAmaxWideThreads), grid_y(batch));
+        if (bf16)
+            hipLaunchKernelGGL((amax_kernel<true, kAmaxWideThreads>), grid, dim3(kAmaxWideThreads), 0, s,
+                               xv, vec, batch, amax);
+        else
+            hipLaunchKernelGGL((amax_kernel<false, kAmaxWideThreads>), grid, dim3(kAmaxWideThreads), 0, s,
+                               xv, vec, batch, amax);
+        return;
+    }
     dim3 grid(groups_per_tensor(vec, batch, kAmaxGroups), grid_y(batch));
     if (bf16)
-        hipLaunchKernelGGL(amax_kernel<true>, grid, dim3(kThreads), 0, s,
-                           static_cast<const uint4*>(x), vec, batch, amax);
+        hipLaunchKernelGGL((amax_kernel<true, kThreads>), grid, dim3(kThreads), 0, s, xv, vec, batch, amax);
     else
-        hipLaunchKernelGGL(amax_kernel<false>, grid, dim3(kThreads), 0, s,
-                           static_cast<const uint4*>(x), vec, batch, amax);
+        hipLaunchKernelGGL((amax_kernel<false, kThreads>), grid, dim3(kThreads), 0, s, xv, vec, batch, amax);
 }
 
 // ---------------------------------------------------------------------------

@@ -178,6 +178,76 @@ def test_quantize_edges(kind, dtype):
                                             Cc).view(np.uint32))
 
 
+@pytest.mark.parametrize("rows,cols,dtype", [
+    (1, 16, "f32"), (3, 48, "bf16"), (517, 96, "bf16"), (300, 80, "f32"),
+    (2048, 16384, "bf16"), (2049, 16400, "bf16"),
+])
+def test_quantize_from_scratch(rows, cols, dtype):
+    """tq_quantize / tq_quantize_guided of one tensor without a given amax (amax pass,
+    then quantize pass).  Bit-exact against the oracle for nearest, hints and guided,
+    tensor amax and tensor scale included, on every element for small tensors and on
+    sampled rows for the large ones."""
+    rng = np.random.default_rng(rows * 7 + cols)
+    x = (rng.standard_t(4, (rows, cols)) * 0.5).astype(np.float32)
+    x[rng.random(x.shape) < 1e-3] *= 40
+    xt = (x * (1 + rng.uniform(-2 ** -8, 2 ** -8, x.shape))).astype(np.float32)
+    if dtype == "bf16":
+        gx, gt = torch.from_numpy(x).to(torch.bfloat16), torch.from_numpy(xt).to(torch.bfloat16)
+    else:
+        gx, gt = torch.from_numpy(x), torch.from_numpy(xt)
+    n = rows * cols
+    hints = torch.zeros(ops.hint_words(n), dtype=torch.int32, device=DEV)
+    qr = ops.quantize(gx.to(DEV), hints_out=hints)
+    qg = ops.quantize_guided(gt.to(DEV), hints)
+    qn = ops.quantize(gt.to(DEV))
+    torch.cuda.synchronize()
+    o_am_r = oracle.tensor_amax(gx, 1, n)
+    o_am_t = oracle.tensor_amax(gt, 1, n)
+    assert npu8(qr.tensor_amax)[0] == o_am_r[0] and npu8(qg.tensor_amax)[0] == o_am_t[0]
+    sel = np.arange(rows) if rows <= 600 else np.unique(np.r_[0, rows - 1, rng.choice(rows, 40)])
+    xs, ts_ = gx[sel].contiguous(), gt[sel].contiguous()
+    R = sel.size
+    o_r = oracle.quantize(xs, 1, R, cols, amax=o_am_r)
+    o_n = oracle.quantize(ts_, 1, R, cols, amax=o_am_t)
+    codes = lambda q: npu8(q.codes).reshape(rows, cols // 2)[sel].reshape(-1)
+    scl = lambda q: npu8(q.scales).reshape(rows, cols // 16)[sel].reshape(-1)
+    assert np.array_equal(codes(qr), o_r["codes"]) and np.array_equal(scl(qr), o_r["scales"])
+    assert npu8(qr.tensor_scale)[0] == o_r["tensor_scale"][0]
+    assert np.array_equal(codes(qn), o_n["codes"]) and np.array_equal(scl(qn), o_n["scales"])
+    # hints of the sampled rows, then guided codes from them
+    hw = hints_np(hints)
+    o_h = oracle.extract_hint(o_r["codes"], R * cols)
+    bits = np.unpackbits(hw.view(np.uint8), bitorder="little")[:n].reshape(rows, cols)[sel].reshape(-1)
+    assert np.array_equal(np.unpackbits(o_h.view(np.uint8), bitorder="little")[:R * cols], bits)
+    o_g = oracle.quantize_guided(ts_, 1, R, cols, o_h, amax=o_am_t)
+    assert np.array_equal(codes(qg), o_g["codes"]) and np.array_equal(scl(qg), o_g["scales"])
+    assert npu8(qg.tensor_scale)[0] == o_g["tensor_scale"][0]
+    if rows <= 600:  # every element, and nothing written past the last hint word
+        assert np.array_equal(hw[:ops.hint_words(n)], oracle.extract_hint(o_r["codes"], n))
+
+
+@pytest.mark.parametrize("batch,n,dtype", [
+    (1, 16, "bf16"), (1, 8 * 2 ** 20 + 48, "bf16"), (3, 4112, "f32"), (255, 1024, "bf16"),
+    (256, 48, "bf16"), (300, 2064, "f32"),
+])
+def test_tensor_amax_batches(batch, n, dtype):
+    """tq_tensor_amax over batches on both sides of the switch between the two launch
+    shapes (1024-thread workgroups below 256 tensors, 256-thread workgroups from 256
+    on), with the maximum at a random place per tensor, some tensors all zero and some
+    holding subnormals only; bit-exact against the oracle."""
+    rng = np.random.default_rng(batch * 131 + n)
+    x = rng.standard_normal((batch, n)).astype(np.float32)
+    where = rng.integers(0, n, batch)
+    x[np.arange(batch), where] = rng.choice([-1, 1], batch) * rng.uniform(3, 300, batch)
+    x[rng.random(batch) < 0.1] = 0.0
+    sub = rng.random(batch) < 0.05
+    x[sub] = np.float32(1e-40) * rng.standard_normal((int(sub.sum()), n)).astype(np.float32)
+    g = torch.from_numpy(x).to(torch.bfloat16) if dtype == "bf16" else torch.from_numpy(x)
+    am = ops.tensor_amax(g.to(DEV), batch=batch)
+    torch.cuda.synchronize()
+    assert np.array_equal(am.cpu().numpy(), oracle.tensor_amax(g, batch, n))
+
+
 def test_amax_given_and_tensor_amax():
     x = torch.from_numpy(_edge_tensor("zero_and_subnormal_blocks")).to(torch.bfloat16)
     B, R, Cc = x.shape
@@ -766,6 +836,20 @@ GEMM_EDGES = [
 @pytest.mark.parametrize("counts,n,k", GEMM_EDGES)
 def test_grouped_gemm_edges(counts, n, k):
     _gemm_check(counts, n, k, strict=False)
+
+
+# More shapes: one, two and three 64-wide K slices per tile, a single row, K far
+# beyond the staged-scale limit (k = 12800, per-slice scale loads), ragged n, empty
+# groups, one large group.
+GEMM_MORE = [
+    ([8], 64, 64), ([5, 0, 7, 1], 64, 128), ([300, 1, 129], 136, 192), ([200], 256, 12800),
+    ([0, 513, 0, 2], 520, 256), ([1000, 24, 3], 132, 640), ([4096], 768, 2048),
+]
+
+
+@pytest.mark.parametrize("counts,n,k", GEMM_MORE)
+def test_grouped_gemm_more_shapes(counts, n, k):
+    _gemm_check(counts, n, k, seed=9, sample=64 if sum(counts) > 2048 else None, strict=False)
 
 
 def test_grouped_gemm_closed_form():
