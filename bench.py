@@ -49,6 +49,9 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 
 LAYERS, EXPERTS, ROWS, COLS = 48, 64, 2048, 768
 TOKENS = 16384
+CONFIG_ROWS = ("tiny_roundtrip", "activations.amax", "activations.nearest_hint", "activations.guided",
+               "activations.nearest_hint_from_scratch", "activations.nearest_from_scratch",
+               "transpose_requant", "grouped_gemm", "grouped_gemm_w4a4")
 
 
 def parse():
@@ -73,7 +76,11 @@ def parse():
     p.add_argument("--traffic-from", nargs="+", metavar="DIR",
                    help="write profiles/hbm_traffic.json from rocprofv3 counter CSVs under DIR "
                         "(read-request and write-request passes) and exit")
-    p.add_argument("--traffic-section", choices=("step", "configs"), default="step")
+    p.add_argument("--traffic-section", default="step",
+                   help="step, or configs/ROW for one configuration row (see --config-row)")
+    p.add_argument("--config-row", metavar="ROW",
+                   help="run only this configuration row (and its set-up), e.g. for one "
+                        "counter pass per row: " + ", ".join(CONFIG_ROWS))
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run one 1 GiB device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -84,6 +91,8 @@ def main():
     if args.traffic_from:
         print(json.dumps(traffic_from(args.traffic_from, args.traffic_section)[args.traffic_section]))
         return
+    if args.config_row is not None and args.config_row not in CONFIG_ROWS:
+        sys.exit(f"--config-row must be one of {', '.join(CONFIG_ROWS)}")
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU; the path has no "
                                    "multi-GPU leg (--gpus must be 1)"}))
@@ -111,7 +120,12 @@ def main():
         line.update(step["line"])
     else:
         line["config"] = {"workload": "per-configuration rows only (no step)"}
-    configs = None if args.no_configs else measure_configs(L, dev, stream, args.reps)
+    if step is not None:
+        line["copy_ceiling"] = copy_ceiling(dev, stream)
+        for ent in line["kernels"].values():
+            if "GB/s" in ent and "frac_hbm_peak" in ent:
+                ent["frac_copy_ceiling"] = round(ent["GB/s"] / line["copy_ceiling"]["GB/s"], 4)
+    configs = None if args.no_configs else measure_configs(L, dev, stream, args.reps, args.config_row)
     extras = None
     if step is not None and not args.no_extras:
         extras = measure_extras(L, dev, stream, *step["extras_args"])
@@ -131,6 +145,21 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     print(json.dumps(line), flush=True)
+
+
+def copy_ceiling(dev, stream, reps=10):
+    """A measured HBM ceiling: torch's device copy of 1 GiB (1 GiB read, 1 GiB
+    written), average of `reps` back-to-back copies timed with events on `stream`;
+    the two buffers together exceed the Infinity Cache."""
+    import torch
+    src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    with torch.cuda.stream(stream):
+        us = _time_phase(stream, lambda: dst.copy_(src), reps)
+    del src, dst
+    moved = 2.0 * (1 << 30)
+    return {"kernel": "torch copy_ (device to device)", "bytes_per_copy": moved, "avg_us": round(us, 2),
+            "GB/s": round(moved / us / 1e3, 1), "frac_hbm_peak": round(moved / us / 1e3 / HBM_PEAK_GBS, 4)}
 
 
 def measure_step(args, L, dev, stream):
@@ -387,46 +416,51 @@ def _time_rotating(stream, call, n_sets, reps):
     return {"avg_us": round(1e3 * e0.elapsed_time(e1) / reps, 2), "calls": reps, "buffer_sets": n_sets}
 
 
-def _config_traffic(kernel):
+def _config_traffic(row, kernel):
     """Counter-measured HBM bytes per call of a configuration row (the sum over its
-    kernels), or None if not measured on the current sources."""
+    kernels, from the counter passes of that row run alone), or None if not
+    measured on the current sources."""
+    if row is None:
+        return None
     tot = 0
     for k in kernel.split(" + "):
-        ent = _traffic_entry("configs", k)
+        ent = _traffic_entry("configs/" + row, k)
         if ent is None:
             return None
         tot += ent["bytes_per_dispatch"]
     return tot
 
 
-def _bw_row(kernel, timing, alg_bytes, moved_bytes=None, note=None):
+def _bw_row(kernel, timing, alg_bytes, moved_bytes=None, note=None, row=None):
+    """A bandwidth-bound configuration row; `row` names its counter section."""
     us = timing["avg_us"]
     gbs = alg_bytes / us / 1e3
-    row = {"kernel": kernel, **timing, "algorithmic_bytes": alg_bytes, "GB/s": round(gbs, 1),
+    out = {"kernel": kernel, **timing, "algorithmic_bytes": alg_bytes, "GB/s": round(gbs, 1),
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": _config_traffic(kernel)}}
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": _config_traffic(row, kernel)}}
     if moved_bytes is not None:
-        row["moved_bytes"] = moved_bytes
-        row["GB/s_moved"] = round(moved_bytes / us / 1e3, 1)
-        row["frac_hbm_peak_moved"] = round(moved_bytes / us / 1e3 / HBM_PEAK_GBS, 4)
+        out["moved_bytes"] = moved_bytes
+        out["GB/s_moved"] = round(moved_bytes / us / 1e3, 1)
+        out["frac_hbm_peak_moved"] = round(moved_bytes / us / 1e3 / HBM_PEAK_GBS, 4)
     if note:
-        row["note"] = note
-    return row
+        out["note"] = note
+    return out
 
 
-def _mfma_row(kernel, timing, flops, note=None):
+def _mfma_row(kernel, timing, flops, note=None, row=None):
+    """An MFMA-bound configuration row; `row` names its counter section."""
     us = timing["avg_us"]
     tf = flops / us / 1e6
-    row = {"kernel": kernel, **timing, "flops": flops, "TFLOP/s": round(tf, 1),
+    out = {"kernel": kernel, **timing, "flops": flops, "TFLOP/s": round(tf, 1),
            "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
-                        "traffic": _config_traffic(kernel)}}
+                        "traffic": _config_traffic(row, kernel)}}
     if note:
-        row["note"] = note
-    return row
+        out["note"] = note
+    return out
 
 
-def measure_configs(L, dev, stream, reps):
+def measure_configs(L, dev, stream, reps, only=None):
     """One row per workload configuration.  Each row times `reps` back-to-back calls
     with HIP events on the launch stream, rotating over buffer sets that together
     exceed the 256 MiB Infinity Cache (average per call):
@@ -438,7 +472,10 @@ def measure_configs(L, dev, stream, reps):
     * transpose-requantize of an 8192 x 8192 NVFP4 tensor, one call per seed, over
       five source tensors;
     * grouped GEMM, 32 experts, Zipf(1.1) counts over 16384 tokens, K 2048, N 768,
-      over three input sets; and the same with NVFP4 activations."""
+      over three input sets; and the same with NVFP4 activations.
+
+    `only` names one row (CONFIG_ROWS) to run alone, with its set-up, e.g. for a
+    counter pass per row."""
     import torch
 
     from fp4_quantization_precision_amd import inputs, ops
@@ -447,145 +484,164 @@ def measure_configs(L, dev, stream, reps):
     sp = C.c_void_p(stream.cuda_stream)
     P = lambda t: C.c_void_p(t.data_ptr()) if t is not None else None
     out = {}
+    want = lambda *rows: only is None or only in rows
 
     def ok(st, what):
         if st != 0:
             raise RuntimeError(f"{what}: {L.tq_status_string(st).decode()}")
 
     # ---- tiny round trip ----
-    xr, xt = (t.to(dev) for t in inputs.tiny_roundtrip())
-    n1 = xr.numel()
-    h1 = torch.empty(ops.hint_words(n1), dtype=torch.int32, device=dev)
-    q1 = [ops.new_nvfp4((1,), 64, 256, dev) for _ in range(3)]
-    c1 = torch.empty((2, 2), dtype=torch.int64, device=dev)
-    pair = torch.empty((2, 2, n1 // 2), dtype=torch.uint8, device=dev)
+    if want("tiny_roundtrip"):
+        xr, xt = (t.to(dev) for t in inputs.tiny_roundtrip())
+        n1 = xr.numel()
+        h1 = torch.empty(ops.hint_words(n1), dtype=torch.int32, device=dev)
+        q1 = [ops.new_nvfp4((1,), 64, 256, dev) for _ in range(3)]
+        c1 = torch.empty((2, 2), dtype=torch.int64, device=dev)
+        pair = torch.empty((2, 2, n1 // 2), dtype=torch.uint8, device=dev)
 
-    def tiny(_):
-        ok(L.tq_quantize(P(xr), TQ_F32, 1, 64, 256, P(q1[0].tensor_amax), P(q1[0].codes),
-                         P(q1[0].scales), P(q1[0].tensor_scale), P(h1), 0, sp), "tiny nearest+hint")
-        ok(L.tq_quantize(P(xt), TQ_F32, 1, 64, 256, P(q1[1].tensor_amax), P(q1[1].codes),
-                         P(q1[1].scales), P(q1[1].tensor_scale), None, 0, sp), "tiny nearest")
-        ok(L.tq_quantize_guided(P(xt), TQ_F32, 1, 64, 256, P(q1[2].tensor_amax), P(h1),
-                                P(q1[2].codes), P(q1[2].scales), P(q1[2].tensor_scale), 0, sp),
-           "tiny guided")
-        ok(L.tq_code_mismatch(P(pair[0]), P(pair[1]), 2, n1, P(c1), sp), "tiny mismatch")
-    t1 = _time_rotating(stream, tiny, 1, reps)
-    out["tiny_roundtrip"] = {
-        "workload": "tiny round trip: 64 x 256 fp32 X_r, X_t = X_r(1+e); nearest + hint, nearest, "
-                    "guided, mismatch counts (7 kernels incl. amax passes and fills)",
-        **t1, "note": "launch-bound; no roofline claim"}
-    del xr, xt, h1, q1, c1, pair
+        def tiny(_):
+            ok(L.tq_quantize(P(xr), TQ_F32, 1, 64, 256, P(q1[0].tensor_amax), P(q1[0].codes),
+                             P(q1[0].scales), P(q1[0].tensor_scale), P(h1), 0, sp), "tiny nearest+hint")
+            ok(L.tq_quantize(P(xt), TQ_F32, 1, 64, 256, P(q1[1].tensor_amax), P(q1[1].codes),
+                             P(q1[1].scales), P(q1[1].tensor_scale), None, 0, sp), "tiny nearest")
+            ok(L.tq_quantize_guided(P(xt), TQ_F32, 1, 64, 256, P(q1[2].tensor_amax), P(h1),
+                                    P(q1[2].codes), P(q1[2].scales), P(q1[2].tensor_scale), 0, sp),
+               "tiny guided")
+            ok(L.tq_code_mismatch(P(pair[0]), P(pair[1]), 2, n1, P(c1), sp), "tiny mismatch")
+        t1 = _time_rotating(stream, tiny, 1, reps)
+        out["tiny_roundtrip"] = {
+            "workload": "tiny round trip: 64 x 256 fp32 X_r, X_t = X_r(1+e); nearest + hint, nearest, "
+                        "guided, mismatch counts (7 kernels incl. amax passes and fills)",
+            **t1, "note": "launch-bound; no roofline claim"}
+        del xr, xt, h1, q1, c1, pair
 
     # ---- activations 32768 x 4096 bf16 ----
-    T3, H3 = 32768, 4096
-    n3 = T3 * H3
-    ar, at, _ = inputs.activations(T3, H3, device=dev)
-    X = (ar, at)
-    hw = ops.hint_words(n3)
-    h3 = [torch.empty(hw, dtype=torch.int32, device=dev) for _ in range(2)]
-    qa = [ops.new_nvfp4((1,), T3, H3, dev) for _ in range(2)]
-    qs = [ops.new_nvfp4((1,), T3, H3, dev) for _ in range(2)]
-    for i in range(2):
-        ok(L.tq_tensor_amax(P(X[i]), TQ_BF16, 1, n3, P(qa[i].tensor_amax), sp), "amax")
+    if want("activations.amax", "activations.nearest_hint", "activations.guided",
+             "activations.nearest_hint_from_scratch", "activations.nearest_from_scratch"):
+        T3, H3 = 32768, 4096
+        n3 = T3 * H3
+        ar, at, _ = inputs.activations(T3, H3, device=dev)
+        X = (ar, at)
+        hw = ops.hint_words(n3)
+        h3 = [torch.empty(hw, dtype=torch.int32, device=dev) for _ in range(2)]
+        qa = [ops.new_nvfp4((1,), T3, H3, dev) for _ in range(2)]
+        qs = [ops.new_nvfp4((1,), T3, H3, dev) for _ in range(2)]
+        for i in range(2):
+            ok(L.tq_tensor_amax(P(X[i]), TQ_BF16, 1, n3, P(qa[i].tensor_amax), sp), "amax")
 
-    def amax(i):
-        ok(L.tq_tensor_amax(P(X[i]), TQ_BF16, 1, n3, P(qs[i].tensor_amax), sp), "amax")
+        def amax(i):
+            ok(L.tq_tensor_amax(P(X[i]), TQ_BF16, 1, n3, P(qs[i].tensor_amax), sp), "amax")
 
-    def nearest_hint(i):
-        ok(L.tq_quantize(P(X[i]), TQ_BF16, 1, T3, H3, P(qa[i].tensor_amax), P(qa[i].codes),
-                         P(qa[i].scales), P(qa[i].tensor_scale), P(h3[i]), TQ_AMAX_GIVEN, sp),
-           "nearest+hint")
+        def nearest_hint(i):
+            ok(L.tq_quantize(P(X[i]), TQ_BF16, 1, T3, H3, P(qa[i].tensor_amax), P(qa[i].codes),
+                             P(qa[i].scales), P(qa[i].tensor_scale), P(h3[i]), TQ_AMAX_GIVEN, sp),
+               "nearest+hint")
 
-    def guided(i):
-        # the trainer copy guided by the rollout's hints, and (alternating) the reverse
-        ok(L.tq_quantize_guided(P(X[1 - i]), TQ_BF16, 1, T3, H3, P(qa[1 - i].tensor_amax), P(h3[i]),
-                                P(qs[i].codes), P(qs[i].scales), P(qs[i].tensor_scale),
-                                TQ_AMAX_GIVEN, sp), "guided")
+        def guided(i):
+            # the trainer copy guided by the rollout's hints, and (alternating) the reverse
+            ok(L.tq_quantize_guided(P(X[1 - i]), TQ_BF16, 1, T3, H3, P(qa[1 - i].tensor_amax), P(h3[i]),
+                                    P(qs[i].codes), P(qs[i].scales), P(qs[i].tensor_scale),
+                                    TQ_AMAX_GIVEN, sp), "guided")
 
-    def scratch_hint(i):
-        ok(L.tq_quantize(P(X[i]), TQ_BF16, 1, T3, H3, P(qs[i].tensor_amax), P(qs[i].codes),
-                         P(qs[i].scales), P(qs[i].tensor_scale), P(h3[i]), 0, sp),
-           "from-scratch nearest+hint")
+        def scratch_hint(i):
+            ok(L.tq_quantize(P(X[i]), TQ_BF16, 1, T3, H3, P(qs[i].tensor_amax), P(qs[i].codes),
+                             P(qs[i].scales), P(qs[i].tensor_scale), P(h3[i]), 0, sp),
+               "from-scratch nearest+hint")
 
-    def scratch(i):
-        ok(L.tq_quantize(P(X[i]), TQ_BF16, 1, T3, H3, P(qs[i].tensor_amax), P(qs[i].codes),
-                         P(qs[i].scales), P(qs[i].tensor_scale), None, 0, sp), "from-scratch nearest")
-    b_q, b_h = n3 * (2 + 0.5 + 1 / 16), n3 / 8
-    act = {"workload": f"activations [{T3} x {H3}] bf16, Student-t(4), 8 outlier channels x50; "
-                       "rollout and trainer copies alternate (268 MiB each)"}
-    act["amax"] = _bw_row("tq::amax_kernel<true, 1024>", _time_rotating(stream, amax, 2, reps), 2.0 * n3)
-    act["nearest_hint"] = _bw_row("tq::quantize_kernel<true, 1>",
-                                  _time_rotating(stream, nearest_hint, 2, reps), b_q + b_h,
-                                  note="tensor amax given")
-    act["guided"] = _bw_row("tq::quantize_kernel<true, 2>", _time_rotating(stream, guided, 2, reps),
-                            b_q + b_h, note="hints of the other copy, tensor amax given")
-    act["nearest_hint_from_scratch"] = _bw_row(
-        "tq::amax_kernel<true, 1024> + tq::quantize_kernel<true, 1>",
-        _time_rotating(stream, scratch_hint, 2, reps), b_q + b_h, b_q + b_h + 2.0 * n3,
-        note="tq_quantize without a given amax: fill, amax pass, quantize pass")
-    act["nearest_from_scratch"] = _bw_row(
-        "tq::amax_kernel<true, 1024> + tq::quantize_kernel<true, 0>",
-        _time_rotating(stream, scratch, 2, reps), b_q, b_q + 2.0 * n3,
-        note="tq_quantize without a given amax: fill, amax pass, quantize pass")
-    out["activations"] = act
-    del ar, at, X, h3, qa, qs
+        def scratch(i):
+            ok(L.tq_quantize(P(X[i]), TQ_BF16, 1, T3, H3, P(qs[i].tensor_amax), P(qs[i].codes),
+                             P(qs[i].scales), P(qs[i].tensor_scale), None, 0, sp), "from-scratch nearest")
+        b_q, b_h = n3 * (2 + 0.5 + 1 / 16), n3 / 8
+        act = {"workload": f"activations [{T3} x {H3}] bf16, Student-t(4), 8 outlier channels x50; "
+                           "rollout and trainer copies alternate (268 MiB each)"}
+        if want("activations.amax"):
+            act["amax"] = _bw_row("tq::amax_kernel<true, 1024>", _time_rotating(stream, amax, 2, reps),
+                                  2.0 * n3, row="activations.amax")
+        if want("activations.nearest_hint"):
+            act["nearest_hint"] = _bw_row("tq::quantize_kernel<true, 1>",
+                                          _time_rotating(stream, nearest_hint, 2, reps), b_q + b_h,
+                                          note="tensor amax given", row="activations.nearest_hint")
+        if want("activations.guided"):
+            for i in range(2):  # the hints it reads
+                nearest_hint(i)
+            act["guided"] = _bw_row("tq::quantize_kernel<true, 2>", _time_rotating(stream, guided, 2, reps),
+                                    b_q + b_h, note="hints of the other copy, tensor amax given",
+                                    row="activations.guided")
+        if want("activations.nearest_hint_from_scratch"):
+            act["nearest_hint_from_scratch"] = _bw_row(
+                "tq::amax_kernel<true, 1024> + tq::quantize_kernel<true, 1>",
+                _time_rotating(stream, scratch_hint, 2, reps), b_q + b_h, b_q + b_h + 2.0 * n3,
+                note="tq_quantize without a given amax: fill, amax pass, quantize pass",
+                row="activations.nearest_hint_from_scratch")
+        if want("activations.nearest_from_scratch"):
+            act["nearest_from_scratch"] = _bw_row(
+                "tq::amax_kernel<true, 1024> + tq::quantize_kernel<true, 0>",
+                _time_rotating(stream, scratch, 2, reps), b_q, b_q + 2.0 * n3,
+                note="tq_quantize without a given amax: fill, amax pass, quantize pass",
+                row="activations.nearest_from_scratch")
+        out["activations"] = act
+        del ar, at, X, h3, qa, qs
 
     # ---- transpose-requantize 8192 x 8192, one call per seed, five source tensors ----
-    R4 = C4_ = 8192
-    n4 = R4 * C4_
-    srcs = []
-    for j in range(5):
-        src = inputs.transpose_source(R4, C4_, device=dev, seed=4 if j == 0 else 40 + j)
-        srcs.append((ops.quantize(src), ops.new_nvfp4((1,), C4_, R4, dev)))
-        del src
+    if want("transpose_requant"):
+        R4 = C4_ = 8192
+        n4 = R4 * C4_
+        srcs = []
+        for j in range(5):
+            src = inputs.transpose_source(R4, C4_, device=dev, seed=4 if j == 0 else 40 + j)
+            srcs.append((ops.quantize(src), ops.new_nvfp4((1,), C4_, R4, dev)))
+            del src
 
-    def sr(i):
-        q, qt = srcs[i % 5]
-        ok(L.tq_requant_transpose_sr(P(q.codes), P(q.scales), P(q.tensor_scale), 1, R4, C4_,
-                                     C.c_uint64(i), P(qt.codes), P(qt.scales), P(qt.tensor_scale),
-                                     sp), "SR transpose")
-    seeds = {"n": 0}
+        def sr(i):
+            q, qt = srcs[i % 5]
+            ok(L.tq_requant_transpose_sr(P(q.codes), P(q.scales), P(q.tensor_scale), 1, R4, C4_,
+                                         C.c_uint64(i), P(qt.codes), P(qt.scales), P(qt.tensor_scale),
+                                         sp), "SR transpose")
+        seeds = {"n": 0}
 
-    def sr_seeded(j):  # a new seed for every call
-        sr(j + 5 * seeds["n"])
-        seeds["n"] += j == 4
-    out["transpose_requant"] = {
-        "workload": f"NVFP4 [{R4} x {C4_}] (nearest-quantized N(0,1) bf16) -> transposed, "
-                    "stochastic-rounding requantize; a new Philox seed per call",
-        **_bw_row("tq::requant_transpose_sr_kernel<false>", _time_rotating(stream, sr_seeded, 5, reps),
-                  n4 * 2 * (0.5 + 1 / 16))}
-    del srcs
+        def sr_seeded(j):  # a new seed for every call
+            sr(j + 5 * seeds["n"])
+            seeds["n"] += j == 4
+        out["transpose_requant"] = {
+            "workload": f"NVFP4 [{R4} x {C4_}] (nearest-quantized N(0,1) bf16) -> transposed, "
+                        "stochastic-rounding requantize; a new Philox seed per call",
+            **_bw_row("tq::requant_transpose_sr_kernel<false>", _time_rotating(stream, sr_seeded, 5, reps),
+                      n4 * 2 * (0.5 + 1 / 16), row="transpose_requant")}
+        del srcs
 
     # ---- grouped GEMM: 32 experts, 16384 tokens, K 2048, N 768, three input sets ----
-    G5, T5, K5, N5 = 32, 16384, 2048, 768
-    sets = []
-    for j in range(3):
-        a5, w5, off5 = inputs.grouped_gemm_inputs(G5, T5, K5, N5, device=dev, seed=5 if j == 0 else 50 + j)
-        sets.append((a5, off5.to(dev), ops.quantize(w5), ops.quantize(a5.view(1, T5, K5)),
-                     torch.empty((T5, N5), dtype=torch.bfloat16, device=dev)))
-        del w5
+    if want("grouped_gemm", "grouped_gemm_w4a4"):
+        G5, T5, K5, N5 = 32, 16384, 2048, 768
+        sets = []
+        for j in range(3):
+            a5, w5, off5 = inputs.grouped_gemm_inputs(G5, T5, K5, N5, device=dev, seed=5 if j == 0 else 50 + j)
+            sets.append((a5, off5.to(dev), ops.quantize(w5), ops.quantize(a5.view(1, T5, K5)),
+                         torch.empty((T5, N5), dtype=torch.bfloat16, device=dev)))
+            del w5
 
-    def gemm(i):
-        a5, off5, q5, _, o5 = sets[i]
-        ok(L.tq_grouped_gemm_nvfp4(P(a5), P(off5), G5, T5, N5, K5, P(q5.codes), P(q5.scales),
-                                   P(q5.tensor_scale), P(o5), sp), "grouped GEMM")
+        def gemm(i):
+            a5, off5, q5, _, o5 = sets[i]
+            ok(L.tq_grouped_gemm_nvfp4(P(a5), P(off5), G5, T5, N5, K5, P(q5.codes), P(q5.scales),
+                                       P(q5.tensor_scale), P(o5), sp), "grouped GEMM")
 
-    def w4a4(i):
-        _, off5, q5, a5q, o5 = sets[i]
-        ok(L.tq_grouped_gemm_w4a4(P(a5q.codes), P(a5q.scales), P(a5q.tensor_scale), P(off5), G5, T5,
-                                  N5, K5, P(q5.codes), P(q5.scales), P(q5.tensor_scale), P(o5), sp),
-           "W4A4 grouped GEMM")
-    flops5 = 2.0 * T5 * K5 * N5
-    out["grouped_gemm"] = {
-        "workload": f"{G5} experts, Zipf(1.1) counts over {T5} tokens, K {K5}, N {N5}; "
-                    "A bf16 N(0,1), W NVFP4 from N(0,0.02)",
-        **_mfma_row("tq::grouped_gemm_nvfp4_kernel<false, true>", _time_rotating(stream, gemm, 3, reps),
-                    flops5)}
-    out["grouped_gemm_w4a4"] = {
-        "workload": "as grouped_gemm, activations NVFP4 (one tensor)",
-        **_mfma_row("tq::grouped_gemm_nvfp4_kernel<true, true>", _time_rotating(stream, w4a4, 3, reps),
-                    flops5)}
-    del sets
+        def w4a4(i):
+            _, off5, q5, a5q, o5 = sets[i]
+            ok(L.tq_grouped_gemm_w4a4(P(a5q.codes), P(a5q.scales), P(a5q.tensor_scale), P(off5), G5, T5,
+                                      N5, K5, P(q5.codes), P(q5.scales), P(q5.tensor_scale), P(o5), sp),
+               "W4A4 grouped GEMM")
+        flops5 = 2.0 * T5 * K5 * N5
+        if want("grouped_gemm"):
+            out["grouped_gemm"] = {
+                "workload": f"{G5} experts, Zipf(1.1) counts over {T5} tokens, K {K5}, N {N5}; "
+                            "A bf16 N(0,1), W NVFP4 from N(0,0.02)",
+                **_mfma_row("tq::grouped_gemm_nvfp4_kernel<false, true>",
+                            _time_rotating(stream, gemm, 3, reps), flops5, row="grouped_gemm")}
+        if want("grouped_gemm_w4a4"):
+            out["grouped_gemm_w4a4"] = {
+                "workload": "as grouped_gemm, activations NVFP4 (one tensor)",
+                **_mfma_row("tq::grouped_gemm_nvfp4_kernel<true, true>",
+                            _time_rotating(stream, w4a4, 3, reps), flops5, row="grouped_gemm_w4a4")}
+        del sets
     torch.cuda.synchronize()
     return out
 
@@ -821,6 +877,8 @@ def traffic_from(dirs, section):
                     per.setdefault(k, {}).setdefault(c, {})[r["Dispatch_Id"]] = float(r["Counter_Value"])
     kernels = {}
     for k, cs in per.items():
+        if not k.startswith("tq::"):  # input generation and other library kernels
+            continue
         need = ("TCC_EA0_RDREQ", "TCC_EA0_RDREQ_32B", "TCC_EA0_WRREQ", "TCC_EA0_WRREQ_64B")
         if not all(c in cs for c in need):
             continue
