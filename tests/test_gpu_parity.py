@@ -840,10 +840,14 @@ def test_grouped_gemm_edges(counts, n, k):
 
 # More shapes: one, two and three 64-wide K slices per tile, a single row, K far
 # beyond the staged-scale limit (k = 12800, per-slice scale loads), ragged n, empty
-# groups, one large group.
+# groups, one large group, and two mid-size problems with a ragged last column
+# tile: [6000, 7000, 400, 3] x 520 (321 tiles, 8 columns in the last column tile)
+# and [9000, 5000, 200] x 1032 (565 tiles, more than one round of the chip's 512
+# workgroup slots).
 GEMM_MORE = [
     ([8], 64, 64), ([5, 0, 7, 1], 64, 128), ([300, 1, 129], 136, 192), ([200], 256, 12800),
     ([0, 513, 0, 2], 520, 256), ([1000, 24, 3], 132, 640), ([4096], 768, 2048),
+    ([6000, 7000, 400, 3], 520, 256), ([9000, 5000, 200], 1032, 192),
 ]
 
 
@@ -914,6 +918,12 @@ def test_w4a4_gemm_forward_shape():
 @pytest.mark.parametrize("counts,n,k", GEMM_EDGES)
 def test_w4a4_gemm_edges(counts, n, k):
     _w4a4_check(counts, n, k, strict=False)
+
+
+@pytest.mark.parametrize("counts,n,k", GEMM_MORE[-2:])
+def test_w4a4_gemm_mid_size(counts, n, k):
+    """The two mid-size GEMM_MORE shapes for the W4A4 kernel."""
+    _w4a4_check(counts, n, k, seed=11, sample=64, strict=False)
 
 
 def test_code_mismatch_random():
