@@ -222,61 +222,87 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
     // modes, when the grid has a multiple of 8 workgroups, they are renumbered
     // so that each XCD streams a contiguous eighth of the launch (3.5% faster on
     // the MoE-weights workload; the guided mode, which also reads the hints,
-    // ran 4.5% slower with it and keeps the plain order).
+    // ran 4.5% slower with it and keeps the plain order).  The renumbering is
+    // scalar and 32-bit unless the grid has 2^32 workgroups or more.
     uint32_t bx = blockIdx.x, by = blockIdx.y;
     if constexpr (MODE != MODE_GUIDED) {
-        const uint64_t G = (uint64_t)gridDim.x * gridDim.y;
+        const uint32_t gx = gridDim.x, gy = gridDim.y;
+        const uint64_t G = (uint64_t)gx * gy;
         if ((G & 7) == 0) {
-            const uint64_t L = (uint64_t)by * gridDim.x + bx;
-            const uint64_t R = (L & 7) * (G >> 3) + (L >> 3);
-            by = (uint32_t)(R / gridDim.x);
-            bx = (uint32_t)(R - (uint64_t)by * gridDim.x);
+            if (gy == 1) {
+                bx = (bx & 7) * (gx >> 3) + (bx >> 3);
+            } else if (G <= 0xFFFFFFFFull) {
+                const uint32_t L = by * gx + bx, R = (L & 7) * (uint32_t)(G >> 3) + (L >> 3);
+                by = R / gx;
+                bx = R - by * gx;
+            } else {
+                const uint64_t L = (uint64_t)by * gx + bx, R = (L & 7) * (G >> 3) + (L >> 3);
+                by = (uint32_t)(R / gx);
+                bx = (uint32_t)(R - (uint64_t)by * gx);
+            }
         }
     }
-    for (int64_t b = by; b < batch; b += gridDim.y) {
+    // block j of tensor b
+    auto quantize_block = [&](int64_t b, int64_t j, float s_t) __attribute__((always_inline)) {
+        const int64_t blk = b * blocks_per_tensor + j;
+        float v[16];
+        load_block<BF16>(x, blk, v);
+        uint32_t hin = 0;
+        if (MODE == MODE_GUIDED)
+            hin = hints[blk];
+        float A_b = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            A_b = fmaxf(A_b, fabsf(v[i]));
+        uint32_t e = 0;
+        if (s_t != 0.0f)
+            e = e4m3_encode((A_b / 6.0f) / s_t);
+        const float dec = e4m3_decode(e);
+        uint32_t lo = 0, hi = 0;
+        if (dec != 0.0f) {
+            const float r_b = 1.0f / (dec * s_t);
+            float y[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                y[i] = v[i] * r_b;
+            if (MODE == MODE_GUIDED) {
+                lo = pack8_guided(y, hin);
+                hi = pack8_guided(y + 8, hin >> 8);
+            } else {
+                lo = pack8_nearest(y);
+                hi = pack8_nearest(y + 8);
+            }
+        }
+        codes[blk] = make_uint2(lo, hi);
+        scales[blk] = (uint8_t)e;
+        if (MODE == MODE_NEAREST_HINT) {
+            hints[blk] = (uint16_t)(parity8(lo) | (parity8(hi) << 8));
+            if ((total_blocks & 1) && blk == total_blocks - 1)
+                hints[blk + 1] = 0;  // zero the unused half of the last word
+        }
+    };
+    auto scale_of = [&](int64_t b) -> float {
         const float A_T = tensor_amax[b];
-        const float s_t = (A_T == 0.0f) ? 0.0f : A_T / 2688.0f;
+        return (A_T == 0.0f) ? 0.0f : A_T / 2688.0f;
+    };
+    // The launcher's usual grid: one workgroup row per tensor and one block per
+    // lane, so no loop.
+    if ((int64_t)gridDim.y == batch && (int64_t)gridDim.x * kThreads >= blocks_per_tensor) {
+        const float s_t = scale_of(by);
+        if (bx == 0 && threadIdx.x == 0)
+            tensor_scale[by] = s_t;
+        const int64_t j = (int64_t)bx * kThreads + threadIdx.x;
+        if (j < blocks_per_tensor)
+            quantize_block(by, j, s_t);
+        return;
+    }
+    for (int64_t b = by; b < batch; b += gridDim.y) {
+        const float s_t = scale_of(b);
         if (bx == 0 && threadIdx.x == 0)
             tensor_scale[b] = s_t;
         for (int64_t j = (int64_t)bx * kThreads + threadIdx.x; j < blocks_per_tensor;
-             j += (int64_t)gridDim.x * kThreads) {
-            const int64_t blk = b * blocks_per_tensor + j;
-            float v[16];
-            load_block<BF16>(x, blk, v);
-            uint32_t hin = 0;
-            if (MODE == MODE_GUIDED)
-                hin = hints[blk];
-            float A_b = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                A_b = fmaxf(A_b, fabsf(v[i]));
-            uint32_t e = 0;
-            if (s_t != 0.0f)
-                e = e4m3_encode((A_b / 6.0f) / s_t);
-            const float dec = e4m3_decode(e);
-            uint32_t lo = 0, hi = 0;
-            if (dec != 0.0f) {
-                const float r_b = 1.0f / (dec * s_t);
-                float y[16];
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    y[i] = v[i] * r_b;
-                if (MODE == MODE_GUIDED) {
-                    lo = pack8_guided(y, hin);
-                    hi = pack8_guided(y + 8, hin >> 8);
-                } else {
-                    lo = pack8_nearest(y);
-                    hi = pack8_nearest(y + 8);
-                }
-            }
-            codes[blk] = make_uint2(lo, hi);
-            scales[blk] = (uint8_t)e;
-            if (MODE == MODE_NEAREST_HINT) {
-                hints[blk] = (uint16_t)(parity8(lo) | (parity8(hi) << 8));
-                if ((total_blocks & 1) && blk == total_blocks - 1)
-                    hints[blk + 1] = 0;  // zero the unused half of the last word
-            }
-        }
+             j += (int64_t)gridDim.x * kThreads)
+            quantize_block(b, j, s_t);
     }
 }
 

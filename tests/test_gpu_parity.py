@@ -260,6 +260,33 @@ def test_amax_given_and_tensor_amax():
     assert_q_equal(g, oracle.quantize(x, B, R, Cc), "amax given")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quantize_more_tensors_than_grid_rows(dtype):
+    """65541 tensors of 2 x 16 values: more tensors than the launch has workgroup rows
+    (65535), so the quantizers take their looping path over tensors.  Nearest with
+    hints, guided and from-scratch amax, bit-exact against the oracle on every
+    tensor."""
+    B, R, Cc = 65541, 2, 16
+    rng = np.random.default_rng(65541)
+    x = (rng.standard_normal((B, R, Cc)) * np.exp2(rng.integers(-20, 20, (B, 1, 1)))).astype(np.float32)
+    x[rng.random(B) < 0.01] = 0.0
+    xt = (x * (1 + rng.uniform(-2 ** -8, 2 ** -8, x.shape))).astype(np.float32)
+    if dtype == "bf16":
+        gx, gt = torch.from_numpy(x).to(torch.bfloat16), torch.from_numpy(xt).to(torch.bfloat16)
+    else:
+        gx, gt = torch.from_numpy(x), torch.from_numpy(xt)
+    n = B * R * Cc
+    hints = torch.zeros(ops.hint_words(n), dtype=torch.int32, device=DEV)
+    qr = ops.quantize(gx.to(DEV), hints_out=hints)
+    qg = ops.quantize_guided(gt.to(DEV), hints)
+    torch.cuda.synchronize()
+    o_r = oracle.quantize(gx, B, R, Cc)
+    assert_q_equal(qr, o_r, "rollout")
+    o_h = oracle.extract_hint(o_r["codes"], n)
+    assert np.array_equal(hints_np(hints), o_h)
+    assert_q_equal(qg, oracle.quantize_guided(gt, B, R, Cc, o_h), "guided")
+
+
 def test_empty_tensors():
     x = torch.zeros((3, 0, 32), dtype=torch.bfloat16, device=DEV)
     out = ops.new_nvfp4((3,), 0, 32, DEV)
