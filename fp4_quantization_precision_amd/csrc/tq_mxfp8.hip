@@ -24,6 +24,10 @@
 
 namespace tq {
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2 as_u16x2(uint32_t x) { return __builtin_bit_cast(u16x2, x); }
+__device__ __forceinline__ uint32_t as_u32(u16x2 x) { return __builtin_bit_cast(uint32_t, x); }
+
 // Shared exponent of a block with maximum magnitude A > 0: floor(log2 A) - 8,
 // clamped to [-127, 127] (frexp handles subnormal A).
 __device__ __forceinline__ int mx_shared_exp(float A)
@@ -199,6 +203,8 @@ __global__ __launch_bounds__(kMThreads, 2) void requant_transpose_mxfp8_sr_kerne
     };
     LRegs R;
     load(blockIdx.x, R);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the first tile is needed at once, and no load
+                                         // is then pending where the loop begins
     for (int64_t tile = blockIdx.x; tile < total_tiles; tile += gridDim.x) {
         const Tile T = tile_of(tile);
         const int64_t b = T.b, r0 = T.r0, c0 = T.c0;
@@ -227,7 +233,7 @@ __global__ __launch_bounds__(kMThreads, 2) void requant_transpose_mxfp8_sr_kerne
                 const float vb[8] = {b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    u_s[mlds_slot(cl + 8 * j + e, p)] = pack_hi16(va[e] * da + 0.0f, vb[e] * db + 0.0f);
+                    u_s[mlds_slot(cl + 8 * j + e, p)] = pack_hi16(va[e] * da, vb[e] * db);
             }
         }
         // the next tile's codes are in flight during this tile's requantization
@@ -238,14 +244,16 @@ __global__ __launch_bounds__(kMThreads, 2) void requant_transpose_mxfp8_sr_kerne
         {
             const int c = tid & (kMTC - 1), half = tid >> 8, h = c >> 5;
             const int64_t oc = c0 + c;
-            if (c < cols_valid) {
+            // Lanes past the tile's columns compute on the zeros staged there and store
+            // nothing: no branch encloses the wait below, which is then on every path.
+            const bool active = c < cols_valid;
+            {
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
                     const int lr = 64 * half + 32 * q;  // first local input row of the block
-                    if (lr >= rows_valid)
-                        continue;
-                    // the block's 32 staged values as bf16 pairs; a sign bit marks a
-                    // nonzero negative value (zeros were staged as +0)
+                    const bool live = lr < rows_valid;
+                    // the block's 32 staged values as bf16 pairs (a zero may carry a
+                    // sign: -0 codes and zero scales stage as -0)
                     uint32_t pk[16];
 #pragma unroll
                     for (int part = 0; part < 2; ++part) {
@@ -261,10 +269,19 @@ __global__ __launch_bounds__(kMThreads, 2) void requant_transpose_mxfp8_sr_kerne
                     auto ubits = [&](int e) -> uint32_t {  // binary32 bits of element e
                         return (e & 1) ? (pk[e >> 1] & 0xFFFF0000u) : (pk[e >> 1] << 16);
                     };
-                    uint32_t Ab = 0;  // |u| bits: integer order = value order
+                    // Every u is exact in bf16, so the low 16 bits of its binary32 pattern
+                    // are zero and the integer steps below run on the 16-bit magnitude
+                    // patterns |u|16, two per packed 16-bit instruction.  Block maximum (the
+                    // integer order of |u| bits is the value order) and smallest nonzero
+                    // |u|16, less one (a zero wraps to 0xFFFF).
+                    u16x2 amax2 = {0, 0}, nzmin2 = {0xFFFF, 0xFFFF};
 #pragma unroll
-                    for (int e = 0; e < 32; ++e)
-                        Ab = max(Ab, ubits(e) & 0x7FFFFFFFu);
+                    for (int j = 0; j < 16; ++j) {
+                        const u16x2 a = as_u16x2(pk[j] & 0x7FFF7FFFu);
+                        amax2 = __builtin_elementwise_max(amax2, a);
+                        nzmin2 = __builtin_elementwise_min(nzmin2, a - (u16x2){1, 1});
+                    }
+                    const uint32_t Ab = (uint32_t)(amax2[0] > amax2[1] ? amax2[0] : amax2[1]) << 16;
                     const int64_t obase = (b * cols + oc) * rows + r0 + lr;  // output linear index
                     uint32_t wout[8] = {0, 0, 0, 0, 0, 0, 0, 0};
                     uint32_t sb = 0;
@@ -279,13 +296,16 @@ __global__ __launch_bounds__(kMThreads, 2) void requant_transpose_mxfp8_sr_kerne
                         // (k < 256 * frac) is "X mod 2^20 > k * 2^12": one carry,
                         // (X + 2^20 - 1 - k * 2^12) >> 20.  Codes past 0x7E clamp
                         // (|y| >= 448 gives 448), and zeros give X = 0 and code 0.
+                        // On 16-bit patterns, X = X16 << 16 with X16 = max(|u|16 - K16, 0)
+                        // and K16 = (se + 120) << 7; X mod 2^20 is a multiple of 2^16, so
+                        // only the high nibble kh of k decides the carry, and the code is
+                        // (min(X16, 0x7E0) + 15 - kh) >> 4 (equal to the 32-bit form for
+                        // every 16-bit pattern and byte, checked exhaustively).
                         const int kexp = se + 120;
-                        uint32_t nzmin = 0xFFFFFFFFu;  // smallest nonzero |u| bits, less one
-#pragma unroll
-                        for (int e = 0; e < 32; ++e)
-                            nzmin = min(nzmin, (ubits(e) & 0x7FFFFFFFu) - 1u);
-                        const bool fast = kexp > 0 && nzmin >= ((uint32_t)(kexp + 1) << 23) - 1u;
-                        const uint32_t K = (uint32_t)kexp << 23;
+                        const uint32_t nzmin = nzmin2[0] < nzmin2[1] ? nzmin2[0] : nzmin2[1];
+                        const bool fast = kexp > 0 && nzmin >= ((uint32_t)(kexp + 1) << 7) - 1u;
+                        const uint16_t K16 = (uint16_t)(kexp > 0 ? kexp << 7 : 0);
+                        const u16x2 KK = {K16, K16};
 #pragma unroll
                         for (int part = 0; part < 2; ++part) {
                             const uint64_t beta = (uint64_t)(obase / 16) + part;
@@ -294,13 +314,29 @@ __global__ __launch_bounds__(kMThreads, 2) void requant_transpose_mxfp8_sr_kerne
                             const uint32_t rw[4] = {rnd.x, rnd.y, rnd.z, rnd.w};
                             if (fast) {
 #pragma unroll
-                                for (int i = 0; i < 16; ++i) {
-                                    const int e = 16 * part + i;
-                                    const uint32_t bits = ubits(e);
-                                    const int32_t X = max((int32_t)((bits & 0x7FFFFFFFu) - K), 0);
-                                    const uint32_t k12 = ((rw[i >> 2] >> (8 * (i & 3))) & 0xFFu) << 12;
-                                    const uint32_t m = min(((uint32_t)X + 0xFFFFFu - k12) >> 20, 0x7Eu);
-                                    wout[e >> 2] |= (m | ((bits >> 24) & 0x80u)) << (8 * (e & 3));
+                                for (int d = 0; d < 4; ++d) {  // elements 16 part + 4d .. + 3
+                                    const int j0 = 8 * part + 2 * d;
+                                    // 15 - kh of the four random bytes, one per byte
+                                    const uint32_t T = ~(rw[d] >> 4) & 0x0F0F0F0Fu;
+                                    uint32_t m[2];
+#pragma unroll
+                                    for (int t = 0; t < 2; ++t) {
+                                        const u16x2 a = as_u16x2(pk[j0 + t] & 0x7FFF7FFFu);
+                                        const u16x2 X = __builtin_elementwise_min(
+                                            __builtin_elementwise_sub_sat(a, KK), (u16x2){0x7E0, 0x7E0});
+                                        // bytes 2t and 2t + 1 of T into the two 16-bit lanes
+                                        const u16x2 kh = as_u16x2(__builtin_amdgcn_perm(
+                                            0u, T, t ? 0x0C030C02u : 0x0C010C00u));
+                                        m[t] = as_u32((X + kh) >> (u16x2){4, 4});
+                                    }
+                                    // the four codes (low byte of each lane), and each value's
+                                    // sign (bit 7 of bytes 1 and 3 of its pair) as bit 7, kept
+                                    // for nonzero codes only (code + 0x7F carries into bit 7
+                                    // iff the code is nonzero; codes are at most 0x7E)
+                                    const uint32_t codes4 = __builtin_amdgcn_perm(m[1], m[0], 0x06040200u);
+                                    const uint32_t sg = __builtin_amdgcn_perm(pk[j0 + 1], pk[j0], 0x07050301u) &
+                                                        0x80808080u;
+                                    wout[4 * part + d] = codes4 | (sg & (codes4 + 0x7F7F7F7Fu));
                                 }
                             } else {
 #pragma unroll
@@ -315,10 +351,18 @@ __global__ __launch_bounds__(kMThreads, 2) void requant_transpose_mxfp8_sr_kerne
                             }
                         }
                     }
-                    uint4* orow = reinterpret_cast<uint4*>(codes_t + obase);
-                    orow[0] = make_uint4(wout[0], wout[1], wout[2], wout[3]);
-                    orow[1] = make_uint4(wout[4], wout[5], wout[6], wout[7]);
-                    scales_t[(b * cols + oc) * sct_pitch + (r0 + lr) / 32] = (uint8_t)sb;
+                    // The next tile's codes were loaded before this phase and have landed
+                    // by now.  Waiting for them here, before the first store and on every
+                    // path, keeps the next dequant from waiting on this tile's stores (the
+                    // vector memory counter covers both).
+                    if (q == 0)
+                        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+                    if (active && live) {
+                        uint4* orow = reinterpret_cast<uint4*>(codes_t + obase);
+                        orow[0] = make_uint4(wout[0], wout[1], wout[2], wout[3]);
+                        orow[1] = make_uint4(wout[4], wout[5], wout[6], wout[7]);
+                        scales_t[(b * cols + oc) * sct_pitch + (r0 + lr) / 32] = (uint8_t)sb;
+                    }
                 }
             }
         }
@@ -363,7 +407,11 @@ void launch_requant_transpose_mxfp8_sr(const uint8_t* codes, const uint8_t* scal
                                tensor_scale_t, batch);
         return;
     }
-    const int64_t g = total < 8192 ? total : 8192;
+    // Persistent: about six tiles per workgroup, between 512 workgroups (two per CU)
+    // and 8192, so that each workgroup's loads of its next tile overlap the current one.
+    int64_t g = total / 6 / 8 * 8;
+    g = g < 512 ? 512 : (g > 8192 ? 8192 : g);
+    g = g < total ? g : total;
     if (total + g < ((int64_t)1 << 32))
         hipLaunchKernelGGL(requant_transpose_mxfp8_sr_kernel<false>, dim3((unsigned)g), dim3(kMThreads),
                            0, s, codes, scales, tensor_scale, batch, rows, cols, (uint32_t)seed,

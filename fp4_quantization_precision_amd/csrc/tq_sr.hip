@@ -14,18 +14,22 @@
 // current one.
 //
 // Load phase: a thread takes a pair of input rows and one 32-column chunk,
-// dequantizes them exactly with gfx950's packed FP4 -> f32 conversion
-// (u = +-G[m] * dec(e) has at most 6 significant bits, so bf16 holds it) and
-// stores each column's two values as one dword into LDS, where tile column c
-// (= output row) is an LDS row.  The row-pair index is XOR-swizzled with four
+// dequantizes them exactly in binary16 (u = +-G[m] * dec(e) has at most 6
+// significant bits and lies in [2^-10, 2688] or is zero, so the packed FP4 ->
+// f16 conversion and one packed f16 multiply by the E4M3 scale, itself an f16
+// value, are exact) and stores each column's two values as one dword into LDS,
+// where tile column c (= output row) is an LDS row.  The row-pair index is XOR-swizzled with four
 // times the column's chunk so that each half-wave's stores hit 32 distinct
 // banks, and the LDS row pitch is 68 dwords so that the 16-byte reads of the
 // next phase are conflict-free as well (their two halves swap places for odd
 // chunks).
 //
 // Requantize phase: a thread owns one output row and four new 16-element
-// blocks: block amax, E4M3 scale, one Philox4x32-10 call for the block's 16
-// random bytes, then the stochastic rounding.  The floor grid point of each
+// blocks: block amax (on the f16 magnitude patterns, whose integer order is the
+// value order), E4M3 scale, one Philox4x32-10 call for the block's 16 random
+// bytes, y = u * r' (one mixed-precision FMA per value, f16 u, with a -0 addend
+// so that it is the rounded product, sign of zero included), then the
+// stochastic rounding.  The floor grid point of each
 // value comes from v_cvt_scalef32_sr_pk_fp4_f32 with a zero seed (which
 // truncates to the grid toward zero, sign kept), its value from the packed
 // decode; the step up is taken iff G[lo] + k * D / 256 < |y| with D the grid
@@ -47,6 +51,16 @@ constexpr int kTC = 256;          // input columns per tile (= output rows)
 constexpr int kSThreads = 512;
 constexpr int kLdsStride = 68;    // dwords per LDS row: 64 row pairs + 4 pad
 
+typedef _Float16 sr_h2 __attribute__((ext_vector_type(2)));
+typedef unsigned short sr_u16x2 __attribute__((ext_vector_type(2)));
+
+// the two E2M1 codes of byte S of w as f16 (exact: every E2M1 value is an f16 value)
+template <int S>
+__device__ __forceinline__ sr_h2 fp4x2_to_h2(uint32_t w)
+{
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, S);
+}
+
 // LDS dword of tile column c, input row pair p.  LDS stores are served 32 lanes at a
 // time over 32 four-byte banks.  A store instruction of the load phase has one
 // column offset within each lane's 32-column chunk, so c * 68 is the same bank for
@@ -62,7 +76,9 @@ __device__ __forceinline__ int lds_slot(int c, int p) { return c * kLdsStride + 
 // equals the nearest rule for 0 <= d <= 464 and gives NaN above (the minimum with 448
 // gives the rule's saturation); v_rcp_f32 with one Newton step equals the correctly
 // rounded reciprocal of
-// all 126 nonzero finite E4M3 values.  d = 0 keeps rcp = 1 (the codes are then zero).
+// all 126 nonzero finite E4M3 values.  d = 0 gives rcp = 0: every y of the block is then
+// +-0, which the stochastic rounding below maps to code 0 whatever the random bytes, so
+// zero-scale blocks need no branch.
 struct BlockScale { uint32_t e; float dec, rcp; };
 __device__ __forceinline__ BlockScale block_scale(float A)
 {
@@ -76,7 +92,8 @@ __device__ __forceinline__ BlockScale block_scale(float A)
     const float dec = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(e, 1.0f, false)[0];
     const float dd = dec == 0.0f ? 1.0f : dec;
     const float r0 = __builtin_amdgcn_rcpf(dd);
-    return {e, dec, __builtin_fmaf(__builtin_fmaf(-dd, r0, 1.0f), r0, r0)};
+    const float r1 = __builtin_fmaf(__builtin_fmaf(-dd, r0, 1.0f), r0, r0);
+    return {e, dec, dec == 0.0f ? 0.0f : r1};
 }
 
 // Stochastic rounding of eight values with their random bytes k[0..7]: floor
@@ -196,6 +213,10 @@ __global__ __launch_bounds__(kSThreads, 2) void requant_transpose_sr_kernel(
             }
         }
     };
+    // -0, hidden from constant folding so that u * r' + (-0) stays one mixed-precision FMA
+    // (its rounded value is that of the product u * r', sign of zero included)
+    float neg_zero = -0.0f;
+    asm("" : "+v"(neg_zero));
     LRegs R;
     load(blockIdx.x, R);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the first tile is needed at once, and no load
@@ -210,25 +231,24 @@ __global__ __launch_bounds__(kSThreads, 2) void requant_transpose_sr_kernel(
         // ---- exact dequant of the prefetched codes into LDS ----
         {
             const int p = lp, cl = lcl;
-            float d[2][2];
+            sr_h2 d[2];
 #pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {  // both scale bytes by the exact E4M3 decode
-                const tq_f32x2 dd = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(R.s[rr], 1.0f, false);
-                d[rr][0] = dd[0];
-                d[rr][1] = dd[1];
-            }
+            for (int rr = 0; rr < 2; ++rr)  // both scale bytes by the exact E4M3 -> f16 decode
+                d[rr] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(R.s[rr], 1.0f, false);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float da = d[0][j >> 1], db = d[1][j >> 1];
-                const tq_f32x2 a0 = fp4x2_to_f32<0>(R.w[0][j]), a1 = fp4x2_to_f32<1>(R.w[0][j]);
-                const tq_f32x2 a2 = fp4x2_to_f32<2>(R.w[0][j]), a3 = fp4x2_to_f32<3>(R.w[0][j]);
-                const tq_f32x2 b0 = fp4x2_to_f32<0>(R.w[1][j]), b1 = fp4x2_to_f32<1>(R.w[1][j]);
-                const tq_f32x2 b2 = fp4x2_to_f32<2>(R.w[1][j]), b3 = fp4x2_to_f32<3>(R.w[1][j]);
-                const float va[8] = {a0[0], a0[1], a1[0], a1[1], a2[0], a2[1], a3[0], a3[1]};
-                const float vb[8] = {b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    u_s[lds_slot(cl + 8 * j + e, p)] = pack_hi16(va[e] * da, vb[e] * db);
+                const sr_h2 da = {d[0][j >> 1], d[0][j >> 1]}, db = {d[1][j >> 1], d[1][j >> 1]};
+                auto stage = [&](auto T) __attribute__((always_inline)) {  // columns 8j + 2t, 8j + 2t + 1
+                    constexpr int t = decltype(T)::value;
+                    const uint32_t wa = __builtin_bit_cast(uint32_t, fp4x2_to_h2<t>(R.w[0][j]) * da);
+                    const uint32_t wb = __builtin_bit_cast(uint32_t, fp4x2_to_h2<t>(R.w[1][j]) * db);
+                    u_s[lds_slot(cl + 8 * j + 2 * t, p)] = __builtin_amdgcn_perm(wb, wa, 0x05040100u);
+                    u_s[lds_slot(cl + 8 * j + 2 * t + 1, p)] = __builtin_amdgcn_perm(wb, wa, 0x07060302u);
+                };
+                stage(std::integral_constant<int, 0>{});
+                stage(std::integral_constant<int, 1>{});
+                stage(std::integral_constant<int, 2>{});
+                stage(std::integral_constant<int, 3>{});
             }
         }
         // the next tile's codes are in flight during this tile's requantization
@@ -246,6 +266,11 @@ __global__ __launch_bounds__(kSThreads, 2) void requant_transpose_sr_kernel(
             uint32_t out[8] = {0, 0, 0, 0, 0, 0, 0, 0};
             uint32_t sc = 0;
             int nvalid = 0;
+            // linear index / 16 of the output row's first element in this tile: the
+            // Philox counter of block q is beta0 + q (rows is a multiple of 16)
+            const uint64_t orow_first = ((uint64_t)b * (uint64_t)cols + (uint64_t)oc) * (uint64_t)rows +
+                                        (uint64_t)(r0 + 64 * half);
+            const uint64_t beta0 = orow_first / 16;
             {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
@@ -259,33 +284,27 @@ __global__ __launch_bounds__(kSThreads, 2) void requant_transpose_sr_kernel(
                     const uint4 v0 = *reinterpret_cast<const uint4*>(blk + 4 * (h & 1));
                     const uint4 v1 = *reinterpret_cast<const uint4*>(blk + 4 * ((h & 1) ^ 1));
                     const uint32_t pk[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-                    float u[16];
+                    sr_u16x2 am = {0, 0};
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        u[2 * i] = bf16_lo(pk[i]);
-                        u[2 * i + 1] = bf16_hi(pk[i]);
-                    }
-                    float A = 0.0f;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        A = fmaxf(A, fabsf(u[i]));
+                    for (int i = 0; i < 8; ++i)
+                        am = __builtin_elementwise_max(am, __builtin_bit_cast(sr_u16x2, pk[i] & 0x7FFF7FFFu));
+                    const float A = (float)__builtin_bit_cast(_Float16, am[0] > am[1] ? am[0] : am[1]);
                     const BlockScale bs = block_scale(A);
                     sc |= bs.e << (8 * q);
-                    const float dec = bs.dec, rcp = bs.rcp;
-                    const uint64_t beta = (uint64_t)(((b * cols + oc) * rows + r0 + lr) / 16);
+                    const float rcp = bs.rcp;
+                    const uint64_t beta = beta0 + (uint64_t)q;
                     const u32x4 rnd = philox4x32_10((uint32_t)beta, (uint32_t)(beta >> 32), 0u, 0u,
                                                     seed_lo, seed_hi);
                     const uint32_t rw[4] = {rnd.x, rnd.y, rnd.z, rnd.w};
                     float yc[16], k[16];
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        yc[i] = u[i] * rcp;
+                        const sr_h2 hv = __builtin_bit_cast(sr_h2, pk[i >> 1]);
+                        yc[i] = __builtin_fmaf((float)hv[i & 1], rcp, neg_zero);
                         k[i] = (float)((rw[i >> 2] >> (8 * (i & 3))) & 0xFFu);
                     }
-                    if (dec != 0.0f) {
-                        out[2 * q] = sr_pack8(yc, k);
-                        out[2 * q + 1] = sr_pack8(yc + 8, k + 8);
-                    }
+                    out[2 * q] = sr_pack8(yc, k);
+                    out[2 * q + 1] = sr_pack8(yc + 8, k + 8);
                 }
             }
             // The next tile's codes were loaded before this phase and have landed.  Waiting
@@ -293,7 +312,7 @@ __global__ __launch_bounds__(kSThreads, 2) void requant_transpose_sr_kernel(
             // from waiting on this tile's stores: the vector memory counter covers both.
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
             if (active) {
-                uint8_t* orow = codes_t + ((b * cols + oc) * rows + r0 + 64 * half) / 2;
+                uint8_t* orow = codes_t + orow_first / 2;
                 uint8_t* srow = scales_t + (b * cols + oc) * sct_pitch + (r0 + 64 * half) / 16;
                 if (nvalid == 4 && vec_out) {
                     reinterpret_cast<uint4*>(orow)[0] = make_uint4(out[0], out[1], out[2], out[3]);

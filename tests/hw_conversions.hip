@@ -253,6 +253,94 @@ __global__ void k_rcp_e4m3(unsigned long long* counts, uint32_t* first)
         atomicAdd(counts + 1, 1ull);
 }
 
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+
+// v_cvt_scalef32_pk_f16_fp4 (scale 1) on all 256 bytes, in each of the four byte
+// positions of the source word: +-G[m] as binary16, -0 for the code of -0
+template <int S>
+__device__ void fp4_f16_one(uint32_t b, unsigned long long* counts, uint32_t* first)
+{
+    const h16x2 hw = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(b << (8 * S), 1.0f, S);
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t c = (b >> (4 * j)) & 0xFu;
+        const float ref = (c & 8u) ? -kG[c & 7u] : kG[c & 7u];
+        const float got = (float)hw[j];
+        if (!(got == ref) || signbit(got) != signbit(ref)) {
+            atomicAdd(counts, 1ull);
+            record(first, b | (uint32_t)(S << 8), __float_as_uint(got), __float_as_uint(ref));
+        }
+    }
+}
+__global__ void k_fp4_decode_f16(unsigned long long* counts, uint32_t* first)
+{
+    const uint32_t b = threadIdx.x;  // 0..255
+    fp4_f16_one<0>(b, counts, first);
+    fp4_f16_one<1>(b, counts, first);
+    fp4_f16_one<2>(b, counts, first);
+    fp4_f16_one<3>(b, counts, first);
+}
+
+// v_cvt_scalef32_pk_f16_fp8 (scale 1) on all 65536 byte pairs: the E4M3 values as
+// binary16 (every finite E4M3 value is one), NaN codes give NaN
+__global__ void k_fp8_decode_f16(unsigned long long* counts, uint32_t* first)
+{
+    const uint32_t w = blockIdx.x * blockDim.x + threadIdx.x;  // 0..65535
+    const h16x2 hw = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t b = (w >> (8 * j)) & 0xFFu;
+        const double ref = e4m3_value(b);
+        const float got = (float)hw[j];
+        const bool ok = isnan(ref) ? isnan(got) : ((double)got == ref && signbit(got) == signbit(ref));
+        if (!ok) {
+            atomicAdd(counts, 1ull);
+            record(first, w, __float_as_uint(got), b);
+        }
+    }
+}
+
+// For every signed E2M1 code m (16) and E4M3 scale byte e (0..0x7E): the binary16
+// product G[m] * dec(e) from v_pk_mul_f16 is exact (checked in fp64), and for each
+// reciprocal r = 1/dec(e') that the SR kernel uses (the correctly rounded one, and 0
+// for e' = 0) the mixed-precision FMA of that f16 value, r and -0 equals the binary32
+// product RN(u * r) with its sign of zero (the fp64 product is exact, so rounding it
+// once to binary32 is the correctly rounded product).  counts[1] counts f16 products
+// that are not exact.
+__global__ void k_f16_scale_products(unsigned long long* counts, uint32_t* first)
+{
+    const uint32_t m = threadIdx.x & 15u, e = blockIdx.x;  // e: 0..126
+    const float G = (m & 8u) ? -kG[m & 7u] : kG[m & 7u];
+    const double dec = e4m3_value(e);
+    const h16x2 g2 = {(_Float16)G, (_Float16)-G};
+    const h16x2 d2 = {(_Float16)dec, (_Float16)dec};
+    const uint32_t uw = __builtin_bit_cast(uint32_t, g2 * d2);  // both halves: +-G * dec
+    for (int j = 0; j < 2; ++j) {
+        const double exact = (j ? -(double)G : (double)G) * dec;
+        const float got = (float)__builtin_bit_cast(h16x2, uw)[j];
+        if ((double)got != exact || signbit(got) != signbit(exact)) {
+            atomicAdd(counts + 1, 1ull);
+            record(first, (m << 8) | e, __float_as_uint(got), 0xFFFFFFFFu);
+        }
+    }
+    float neg_zero = -0.0f;
+    asm("" : "+v"(neg_zero));
+    for (uint32_t e2 = threadIdx.x >> 4; e2 <= 0x7Eu; e2 += blockDim.x >> 4) {
+        const double d = e4m3_value(e2);
+        const float r = e2 == 0u ? 0.0f : (float)(1.0 / d);
+        uint32_t uwl = uw;
+        asm("" : "+v"(uwl));  // keeps the f16 -> f32 step inside the FMA, as in the kernel
+        const h16x2 hv = __builtin_bit_cast(h16x2, uwl);
+        const float y[2] = {__builtin_fmaf((float)hv[0], r, neg_zero), __builtin_fmaf((float)hv[1], r, neg_zero)};
+        for (int j = 0; j < 2; ++j) {
+            const double exact = (j ? -(double)G : (double)G) * dec;
+            const float ref = (float)(exact * (double)r);
+            if (__float_as_uint(y[j]) != __float_as_uint(ref)) {
+                atomicAdd(counts, 1ull);
+                record(first, (j << 24) | (m << 16) | (e << 8) | e2, __float_as_uint(y[j]), __float_as_uint(ref));
+            }
+        }
+    }
+}
+
 }  // namespace
 
 #define HWC_ENTRY(name, kernel, grid, block)                                                      \
@@ -270,3 +358,6 @@ HWC_ENTRY(hwc_fp8_decode, k_fp8_decode, 256, 256)
 HWC_ENTRY(hwc_fp8_nearest, k_fp8_nearest, 65536, 256)
 HWC_ENTRY(hwc_div6, k_div6, 65536, 256)
 HWC_ENTRY(hwc_rcp_e4m3, k_rcp_e4m3, 1, 128)
+HWC_ENTRY(hwc_fp4_decode_f16, k_fp4_decode_f16, 1, 256)
+HWC_ENTRY(hwc_fp8_decode_f16, k_fp8_decode_f16, 256, 256)
+HWC_ENTRY(hwc_f16_scale_products, k_f16_scale_products, 127, 256)

@@ -81,3 +81,27 @@ def test_rcp_newton_e4m3():
     (bad, rcp_alone_bad), f = _run("hwc_rcp_e4m3")
     assert bad == 0, f"byte {f[1]:#x}: got {f[2]:#010x}, correctly rounded {f[3]:#010x}"
     assert rcp_alone_bad > 0
+
+
+def test_fp4_decode_f16_all_bytes():
+    """v_cvt_scalef32_pk_f16_fp4 (scale 1) gives +-G[m] as binary16, -0 for the code of
+    -0, for all 256 bytes in each byte position of its source word: the NVFP4 transpose
+    stages its dequantized values in binary16."""
+    (bad, _), f = _run("hwc_fp4_decode_f16")
+    assert bad == 0, f"byte/position {f[1]:#x}: got {f[2]:#010x}, rule {f[3]:#010x}"
+
+
+def test_fp8_decode_f16_all_byte_pairs():
+    """v_cvt_scalef32_pk_f16_fp8 is the exact E4M3 decode into binary16 for all 65536
+    byte pairs (every finite E4M3 value is a binary16 value)."""
+    (bad, _), f = _run("hwc_fp8_decode_f16")
+    assert bad == 0, f"pair {f[1]:#06x}: got {f[2]:#010x} for byte {f[3]:#x}"
+
+
+def test_f16_scale_products_and_mixed_fma():
+    """For every signed E2M1 code and E4M3 scale, the binary16 product G * dec is exact;
+    and the mixed-precision FMA of that f16 value with each reciprocal the SR transpose
+    uses (and 0) and a -0 addend is the binary32 product u * r, sign of zero included."""
+    (bad, inexact), f = _run("hwc_f16_scale_products")
+    assert inexact == 0, f"code/scale {f[1]:#x}: f16 product {f[2]:#010x} is not exact"
+    assert bad == 0, f"case {f[1]:#x}: got {f[2]:#010x}, product {f[3]:#010x}"
