@@ -722,6 +722,38 @@ def test_transpose_sr_on_grid_exact():
         assert np.all(npu8(t.scales) == 0x38)
 
 
+def test_transpose_sr_block_scale_rounds_to_zero():
+    """New blocks whose largest value is nonzero but so small that A/6 rounds to the
+    E4M3 code 0 (every input scale 2^-9 and every code of magnitude 0 or 0.5 in a band
+    of 16 rows, so A <= 2^-10), next to all-zero new blocks (zero codes under a nonzero
+    scale, -0 codes included): scale byte 0 and codes 0 for both, whatever the random
+    bytes, and the rest of the tensor bit-exact."""
+    B, R, Cc = 1, 64, 96
+    rng = np.random.default_rng(23)
+    codes4 = rng.integers(0, 16, size=(R, Cc), dtype=np.uint8)
+    codes4[16:32, :] = rng.choice(np.array([0, 1, 8, 9], dtype=np.uint8), size=(16, Cc))
+    codes4[16, :] = 1                                       # A = 2^-10 > 0 in every column
+    codes4[48:64, :] = rng.choice(np.array([0, 8], dtype=np.uint8), size=(16, Cc))
+    packed = (codes4[:, 0::2] | (codes4[:, 1::2] << 4)).astype(np.uint8).reshape(-1)
+    scales = rng.integers(0x30, 0x50, size=(R, Cc // 16), dtype=np.uint8)
+    scales[16:32, :] = 0x01                                 # 2^-9, the smallest E4M3 value
+    c = torch.from_numpy(packed)
+    s = torch.from_numpy(scales.reshape(-1).copy())
+    ts = torch.ones(1, dtype=torch.float32)
+    q = ops.NVFP4(c.to(DEV), s.to(DEV), ts.to(DEV), torch.zeros(B, device=DEV))
+    for seed in range(3):
+        t = ops.requant_transpose_sr(q, B, R, Cc, seed=seed)
+        torch.cuda.synchronize()
+        o = oracle.requant_transpose_sr(c, s, ts, B, R, Cc, seed)
+        assert np.array_equal(npu8(t.codes), o["codes"]), f"seed {seed}"
+        assert np.array_equal(npu8(t.scales), o["scales"]), f"seed {seed}"
+        sc = npu8(t.scales).reshape(Cc, R // 16)
+        cd = npu8(t.codes).reshape(Cc, R // 2)
+        assert np.all(sc[:, 1] == 0) and np.all(sc[:, 3] == 0)
+        assert np.all(cd[:, 8:16] == 0) and np.all(cd[:, 24:32] == 0)
+        assert np.all(sc[:, 0] != 0)
+
+
 def test_transpose_sr_64_seeds_unbiased():
     """All 64 seeds on a 1024x1024 tensor nearest-quantized from N(0,1): bit-exact
     against the oracle, and the mean over seeds of the requantized values tracks
