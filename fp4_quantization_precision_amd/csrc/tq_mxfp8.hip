@@ -247,6 +247,17 @@ __global__ __launch_bounds__(kMThreads, 2) void requant_transpose_mxfp8_sr_kerne
             // Lanes past the tile's columns compute on the zeros staged there and store
             // nothing: no branch encloses the wait below, which is then on every path.
             const bool active = c < cols_valid;
+            // This wave's lanes are 64 consecutive output rows (one half of each); its
+            // LDS reads below touch only those rows' dwords [32 half, 32 half + 32), which
+            // no other wave reads, so it stages its output codes there: piece p (16
+            // bytes, input rows 64 half + 16 p ..) of row c at dword 8 (p ^ x), x = c >> 6
+            // being the XOR the block reads use (uniform over the wave).  Block q's
+            // pieces go where block q was read from, once it has been read.  Rows of 68
+            // dwords put the staging writes (eight rows, one piece) and the read-back
+            // (two rows, four pieces) on eight distinct 4-bank groups.
+            uint32_t* const stage = u_s + c * kMLdsStride + 32 * half;
+            const int xs = c >> 6;
+            uint32_t sbq[2] = {0, 0};
             {
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
@@ -351,19 +362,40 @@ __global__ __launch_bounds__(kMThreads, 2) void requant_transpose_mxfp8_sr_kerne
                             }
                         }
                     }
-                    // The next tile's codes were loaded before this phase and have landed
-                    // by now.  Waiting for them here, before the first store and on every
-                    // path, keeps the next dequant from waiting on this tile's stores (the
-                    // vector memory counter covers both).
-                    if (q == 0)
-                        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-                    if (active && live) {
-                        uint4* orow = reinterpret_cast<uint4*>(codes_t + obase);
-                        orow[0] = make_uint4(wout[0], wout[1], wout[2], wout[3]);
-                        orow[1] = make_uint4(wout[4], wout[5], wout[6], wout[7]);
-                        scales_t[(b * cols + oc) * sct_pitch + (r0 + lr) / 32] = (uint8_t)sb;
-                    }
+                    *reinterpret_cast<uint4*>(stage + 8 * ((2 * q) ^ xs)) =
+                        make_uint4(wout[0], wout[1], wout[2], wout[3]);
+                    *reinterpret_cast<uint4*>(stage + 8 * ((2 * q + 1) ^ xs)) =
+                        make_uint4(wout[4], wout[5], wout[6], wout[7]);
+                    sbq[q] = live ? sb : 0u;
                 }
+            }
+            // Read the staged codes back so that four lanes write one row's 64 bytes
+            // (16 rows per store instruction): lane l takes piece l % 4 of row
+            // 16 j + l / 4 of the wave's 64.  LDS operations of one wave complete in
+            // order; the fences keep the compiler from moving the reads above the writes.
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int pl = lane & 3, cw = c - lane;  // cw: the wave's first row
+            const bool live_p = 64 * half + 32 * (pl >> 1) < rows_valid;
+            // The next tile's codes were loaded before this phase and have landed by
+            // now.  Waiting for them here, before the first store and on every path,
+            // keeps the next dequant from waiting on this tile's stores (the vector
+            // memory counter covers both).
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {  // one piece at a time: no registers held across
+                const int cr = cw + 16 * j + (lane >> 2);
+                const uint4 v = *reinterpret_cast<const uint4*>(u_s + cr * kMLdsStride + 32 * half + 8 * (pl ^ xs));
+                if (cr < cols_valid && live_p)
+                    *reinterpret_cast<uint4*>(codes_t + (b * cols + c0 + cr) * rows + r0 + 64 * half + 16 * pl) = v;
+            }
+            if (active) {
+                uint8_t* srow = scales_t + (b * cols + oc) * sct_pitch + (r0 + 64 * half) / 32;
+                if (64 * half < rows_valid)
+                    srow[0] = (uint8_t)sbq[0];
+                if (64 * half + 32 < rows_valid)
+                    srow[1] = (uint8_t)sbq[1];
             }
         }
         __syncthreads();
