@@ -155,8 +155,8 @@ __device__ __forceinline__ void transpose8x8_nibbles(uint32_t r[8])
 // Load: a thread takes two 8 x 8 nibble blocks (one dword from each of 8 input
 // rows; the 32 lanes of a half-wave read 128 contiguous bytes of a row) and
 // transposes them in registers; the transposed dwords go to LDS, where an
-// output row (input column) is an LDS row of 16 dwords.  Store: a thread
-// writes one output row's 64 bytes.
+// output row (input column) is an LDS row of 16 dwords.  Store: four lanes
+// write one output row's 64 bytes, 16 bytes each.
 constexpr int kRR = 128, kRC = 256, kTPitch = 17;  // LDS dwords per output row (16 + 1 pad)
 
 __global__ __launch_bounds__(kT16Threads) void transpose_tile16_kernel(
@@ -206,20 +206,20 @@ __global__ __launch_bounds__(kT16Threads) void transpose_tile16_kernel(
                 t_s[(8 * j + q) * kTPitch + i] = v[q];
         }
         __syncthreads();
-        // store: thread -> output row c0 + c (input column), input rows r0 .. r0 + rows_valid
-        {
-            const int c = tid;
-            if (c < cols_valid) {
-                uint32_t* dst = reinterpret_cast<uint32_t*>(codes_t + ((b * cols + c0 + c) * rows + r0) / 2);
-                const uint32_t* row = t_s + c * kTPitch;
-                if (vec16 && rows_valid == kRR) {
+        // store: four lanes per output row (input column c0 + c), each 16 bytes = 32
+        // input rows, so that one store instruction writes 16 rows' 64-byte runs
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        reinterpret_cast<uint4*>(dst)[q] =
-                            make_uint4(row[4 * q], row[4 * q + 1], row[4 * q + 2], row[4 * q + 3]);
+        for (int pass = 0; pass < kRC / (kT16Threads / 4); ++pass) {
+            const int c = (kT16Threads / 4) * pass + (tid >> 2), p = tid & 3;
+            if (c < cols_valid && 32 * p < rows_valid) {
+                const uint32_t* row = t_s + c * kTPitch + 4 * p;
+                uint8_t* dst = codes_t + ((b * cols + c0 + c) * rows + r0) / 2 + 16 * p;
+                if (vec16 && 32 * p + 32 <= rows_valid) {
+                    *reinterpret_cast<uint4*>(dst) = make_uint4(row[0], row[1], row[2], row[3]);
                 } else {
-                    for (int q = 0; q < rows_valid / 16; ++q)
-                        reinterpret_cast<uint2*>(dst)[q] = make_uint2(row[2 * q], row[2 * q + 1]);
+                    reinterpret_cast<uint2*>(dst)[0] = make_uint2(row[0], row[1]);
+                    if (32 * p + 16 < rows_valid)
+                        reinterpret_cast<uint2*>(dst)[1] = make_uint2(row[2], row[3]);
                 }
             }
         }
