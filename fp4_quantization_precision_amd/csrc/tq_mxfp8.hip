@@ -10,10 +10,12 @@
 // [-127, 127]; elements saturate at 448; zero is +0.
 //
 // Quantize: one lane per 32-value block (64 bytes of bf16 in, 32 code bytes and
-// one scale byte out), E4M3 bytes from the packed hardware conversion.  Transpose: tiles of 128 input rows x 256 input columns
-// staged through LDS exactly as in the NVFP4 transpose; each thread then owns
-// one output row and two new blocks of 32 (its 64 values of the tile), with
-// two Philox4x32-10 calls per block for the 32 random bytes.
+// one scale byte out), E4M3 bytes from the packed hardware conversion.
+// Transpose: tiles of 128 input rows x 256 input columns staged through LDS as
+// in the NVFP4 transpose (as bf16 pairs here); each thread then owns one output
+// row and two new blocks of 32 (its 64 values of the tile), with two
+// Philox4x32-10 calls per block for the 32 random bytes, and the codes go back
+// through the wave's own LDS rows so that four lanes store one row's 64 bytes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

@@ -18,24 +18,24 @@
 // significant bits and lies in [2^-10, 2688] or is zero, so the packed FP4 ->
 // f16 conversion and one packed f16 multiply by the E4M3 scale, itself an f16
 // value, are exact) and stores each column's two values as one dword into LDS,
-// where tile column c (= output row) is an LDS row.  The row-pair index is XOR-swizzled with four
-// times the column's chunk so that each half-wave's stores hit 32 distinct
-// banks, and the LDS row pitch is 68 dwords so that the 16-byte reads of the
-// next phase are conflict-free as well (their two halves swap places for odd
-// chunks).
+// where tile column c (= output row) is an LDS row.  The row-pair index is
+// XOR-swizzled with four times the column's chunk so that each half-wave's
+// stores hit 32 distinct banks, and the LDS row pitch is 68 dwords so that the
+// 16-byte reads of the next phase are conflict-free as well (their two halves
+// swap places for odd chunks).
 //
 // Requantize phase: a thread owns one output row and four new 16-element
 // blocks: block amax (on the f16 magnitude patterns, whose integer order is the
 // value order), E4M3 scale, one Philox4x32-10 call for the block's 16 random
 // bytes, y = u * r' (one mixed-precision FMA per value, f16 u, with a -0 addend
 // so that it is the rounded product, sign of zero included), then the
-// stochastic rounding.  The floor grid point of each
-// value comes from v_cvt_scalef32_sr_pk_fp4_f32 with a zero seed (which
-// truncates to the grid toward zero, sign kept), its value from the packed
-// decode; the step up is taken iff G[lo] + k * D / 256 < |y| with D the grid
-// spacing above G[lo] (all terms exact).  Values above 6 in magnitude (the
-// E4M3 block scale may round down) truncate to the top code, whose step up is
-// masked off, so saturation needs no per-value clamp.
+// stochastic rounding.  The floor grid point of each value comes from
+// v_cvt_scalef32_sr_pk_fp4_f32 with a zero seed (which truncates to the grid
+// toward zero, sign kept), its value from the packed decode; the step up is
+// taken iff G[lo] + k * D / 256 < |y| with D the grid spacing above G[lo] (all
+// terms exact).  Values above 6 in magnitude (the E4M3 block scale may round
+// down) truncate to the top code, whose step up is masked off, so saturation
+// needs no per-value clamp.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

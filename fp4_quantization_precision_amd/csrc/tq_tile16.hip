@@ -70,9 +70,9 @@ __device__ __forceinline__ uint32_t row16_max(uint32_t v)
 // unit.
 template <bool BF16, bool WIDE>
 __global__ __launch_bounds__(kT16Threads) void quantize_tile16_kernel(
-    const void* __restrict__ x, int64_t batch, int64_t rows, int64_t cols,
-    const float* __restrict__ tensor_amax, uint2* __restrict__ codes, uint8_t* __restrict__ scales,
-    float* __restrict__ tensor_scale, int64_t units)
+    const void* __restrict__ x, int64_t rows, int64_t cols, const float* __restrict__ tensor_amax,
+    uint2* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ tensor_scale,
+    int64_t units)
 {
     typedef typename std::conditional<WIDE, uint64_t, uint32_t>::type I;
     const int lane = threadIdx.x & 63, t = lane >> 4, j = lane & 15;
@@ -251,7 +251,7 @@ void launch_quantize_tile16(const void* x, bool bf16, int64_t batch, int64_t row
     const bool wide = units + 4 * blocks >= (int64_t(1) << 32) || batch * (rows / 16) * (cols / 16) >= (int64_t(1) << 32);
 #define TQ_T16_LAUNCH(B, W)                                                                        \
     hipLaunchKernelGGL((quantize_tile16_kernel<B, W>), dim3((unsigned)blocks), dim3(kT16Threads), 0, s, \
-                       x, batch, rows, cols, tensor_amax, c2, scales, tensor_scale, units)
+                       x, rows, cols, tensor_amax, c2, scales, tensor_scale, units)
     if (bf16) {
         if (wide)
             TQ_T16_LAUNCH(true, true);
