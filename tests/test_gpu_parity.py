@@ -393,6 +393,72 @@ def test_moe_weights_layer_full_size(layer):
           f" -> {'guided' if with_hints else 'nearest'} {a[0] / n:.3e}")
 
 
+def test_moe_step_launches():
+    """The step's streaming launches at full size: 48 layers x 64 experts of
+    [2048 x 768] bf16 in one call each (3072 tensors, 4.8e9 values, so flattened
+    indices pass 2^32), as the benchmark issues them: tensor amax of both copies,
+    nearest quantize of the rollout copy (layers 0-23) and nearest + hints (layers
+    24-47, 1536 tensors), nearest of the trainer copy over all 48 layers, guided
+    over layers 24-47 with those hints, and both mismatch counts.  Sampled tensors
+    (first, middle and last of each launch) are bit-exact against the oracle,
+    computed on that tensor alone."""
+    L, E, R, Cc = 48, 64, 2048, 768
+    fh = ops.hint_first_layer(L)
+    XR = torch.empty((L, E, R, Cc), dtype=torch.bfloat16, device=DEV)
+    XT = torch.empty_like(XR)
+    for layer in range(L):
+        XR[layer], XT[layer] = inputs.moe_expert_weights_layer(layer, E, R, Cc, device=DEV)
+    per = R * Cc
+    n_h = (L - fh) * E * per
+    QR = ops.new_nvfp4((L, E), R, Cc, DEV)
+    QN = ops.new_nvfp4((L, E), R, Cc, DEV)
+    QG = ops.new_nvfp4((L - fh, E), R, Cc, DEV)
+    H = torch.zeros(ops.hint_words(n_h), dtype=torch.int32, device=DEV)
+    ops.tensor_amax(XR, QR.tensor_amax, batch=L * E)
+    # layers [a, b) of a batch: codes and scales are [L][E][...], the scalars flat [L * E]
+    sub = lambda q, a, b: ops.NVFP4(q.codes[a:b], q.scales[a:b], q.tensor_scale[a * E:b * E],
+                                    q.tensor_amax[a * E:b * E])
+    ops.quantize(XR[:fh], out=sub(QR, 0, fh), amax_given=True)
+    ops.quantize(XR[fh:], out=sub(QR, fh, L), hints_out=H, amax_given=True)
+    ops.tensor_amax(XT, QN.tensor_amax, batch=L * E)
+    ops.quantize(XT, out=QN, amax_given=True)
+    QG.tensor_amax.copy_(QN.tensor_amax[fh * E:])
+    ops.quantize_guided(XT[fh:], H, out=QG, amax_given=True)
+    cnt_n = ops.code_mismatch(QR.codes.reshape(-1), QN.codes.reshape(-1), L * E, per)
+    cnt_g = ops.code_mismatch(QR.codes[fh:].reshape(-1), QG.codes.reshape(-1), (L - fh) * E, per)
+    torch.cuda.synchronize()
+    flat = lambda t: t.reshape(-1)
+    ar_all, an_all = QR.tensor_amax.reshape(-1).cpu(), QN.tensor_amax.reshape(-1).cpu()
+    for t in [0, 1537, L * E - 1]:  # one 3072-tensor launch index each
+        layer, e = divmod(t, E)
+        xr, xt = XR[layer, e].cpu(), XT[layer, e].cpu()
+        assert ar_all[t].item() == xr.float().abs().max().item(), f"rollout amax {t}"
+        assert an_all[t].item() == xt.float().abs().max().item(), f"trainer amax {t}"
+        o_r = oracle.quantize(xr, 1, R, Cc)
+        o_n = oracle.quantize(xt, 1, R, Cc)
+        assert np.array_equal(npu8(flat(QR.codes[layer, e])), o_r["codes"]), f"rollout codes {t}"
+        assert np.array_equal(npu8(flat(QR.scales[layer, e])), o_r["scales"]), f"rollout scales {t}"
+        assert np.array_equal(npu8(flat(QN.codes[layer, e])), o_n["codes"]), f"trainer codes {t}"
+        assert np.array_equal(npu8(flat(QN.scales[layer, e])), o_n["scales"]), f"trainer scales {t}"
+        assert np.array_equal(npu8(QN.tensor_scale[t:t + 1]), o_n["tensor_scale"])
+        o_c = oracle.code_mismatch(o_r["codes"], o_n["codes"], 1, per)
+        assert np.array_equal(cnt_n[t].cpu().numpy().astype(np.uint64), o_c[0]), f"mismatch {t}"
+    h_all = hints_np(H)
+    for tr in [0, 777, (L - fh) * E - 1]:  # index in the 1536-tensor launches
+        t = fh * E + tr
+        layer, e = divmod(t, E)
+        xr, xt = XR[layer, e].cpu(), XT[layer, e].cpu()
+        o_r = oracle.quantize(xr, 1, R, Cc)
+        o_h = oracle.extract_hint(o_r["codes"], per)
+        assert np.array_equal(h_all[tr * per // 32:(tr + 1) * per // 32], o_h), f"hints {tr}"
+        o_g = oracle.quantize_guided(xt, 1, R, Cc, o_h)
+        ql, qe = divmod(tr, E)
+        assert np.array_equal(npu8(flat(QG.codes[ql, qe])), o_g["codes"]), f"guided codes {tr}"
+        assert np.array_equal(npu8(flat(QG.scales[ql, qe])), o_g["scales"]), f"guided scales {tr}"
+        o_c = oracle.code_mismatch(o_r["codes"], o_g["codes"], 1, per)
+        assert np.array_equal(cnt_g[tr].cpu().numpy().astype(np.uint64), o_c[0]), f"guided mismatch {tr}"
+
+
 # ----------------------------------------------------------------------------------
 # Activations: 32768 x 4096 bf16, Student-t(4) with 8 outlier channels
 # ----------------------------------------------------------------------------------
