@@ -29,17 +29,25 @@ constexpr int kThreads = 256;
 //    tensor this measured 5.69 TB/s against 5.08 TB/s with 1024 workgroups of 256
 //    (268 MB); for 25 MB it took 10.1 us against 18.7 us.
 //
-// The kernels that also write (quantize, mismatch) run fastest with one work item
-// per lane and no grid-stride reuse, because consecutive workgroups then cover
-// consecutive memory (measured on MI355X: 5.3 -> 5.8 TB/s for the nearest quantizer
-// between 128k workgroups and one block per lane).  Nontemporal loads for the
-// read-once streams were measured and not kept.
+// The quantizers, which also write, run fastest with one work item per lane and no
+// grid-stride reuse, because consecutive workgroups then cover consecutive memory
+// (measured on MI355X: 5.3 -> 5.8 TB/s for the nearest quantizer between 128k
+// workgroups and one block per lane).  Nontemporal loads for the read-once streams
+// were measured and not kept.
+//
+// The mismatch count only reads, and ends each workgroup with two 64-bit atomics on
+// its tensor's counters; atomics on one address serialize (about 8-12 ns each on
+// MI355X).  Each lane keeps 8 pairs of 16-byte loads in flight and a tensor gets at
+// most 512 workgroups: 3072 tensors of 1.57M codes went from 1111 to 771 us (78% of
+// HBM peak) and one 134M-code tensor from 400 to 38 us against one pair per lane.
 constexpr int64_t kAmaxGroups = 1024;      // 256-thread workgroups, many tensors
 constexpr int64_t kAmaxWideGroups = 256;   // 1024-thread workgroups, fewer tensors
 constexpr int64_t kAmaxWideBelowBatch = 256;
 constexpr int kAmaxWideThreads = 1024;
 constexpr int kAmaxUnroll = 4;
 constexpr int64_t kQuantGroups = (int64_t)1 << 30;  // as many as there are work items
+constexpr int kMismatchUnroll = 8;
+constexpr unsigned kMismatchMaxGroups = 512;  // per tensor
 
 // ---------------------------------------------------------------------------
 // small fills (used instead of memset nodes, which misbehave under graph replay)
@@ -478,6 +486,17 @@ __device__ __forceinline__ void count_word(uint32_t a, uint32_t b, uint32_t& mis
     }
 }
 
+// Both counts over one 16-byte piece (32 codes); equal pieces cost one compare.
+__device__ __forceinline__ void count_vec(uint4 qa, uint4 qb, uint32_t& mism, uint32_t& adj)
+{
+    if (((qa.x ^ qb.x) | (qa.y ^ qb.y) | (qa.z ^ qb.z) | (qa.w ^ qb.w)) == 0u)
+        return;
+    count_word(qa.x, qb.x, mism, adj);
+    count_word(qa.y, qb.y, mism, adj);
+    count_word(qa.z, qb.z, mism, adj);
+    count_word(qa.w, qb.w, mism, adj);
+}
+
 __global__ __launch_bounds__(kThreads) void mismatch_kernel(const uint4* __restrict__ a,
                                                             const uint4* __restrict__ b,
                                                             int64_t vec_per_tensor, int64_t batch,
@@ -486,15 +505,25 @@ __global__ __launch_bounds__(kThreads) void mismatch_kernel(const uint4* __restr
     __shared__ uint32_t red[2][kThreads / 64];
     for (int64_t t = blockIdx.y; t < batch; t += gridDim.y) {
         uint32_t mism = 0, adj = 0;
+        const uint4* ta = a + t * vec_per_tensor;
+        const uint4* tb = b + t * vec_per_tensor;
+        const int64_t stride = (int64_t)gridDim.x * kThreads, last = vec_per_tensor - 1;
+        // All kMismatchUnroll pairs are issued before the first is compared.  Indices
+        // past the end load the last pair (in bounds, unconditional, so that the loads
+        // stay together for any size) and are not counted.
         for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < vec_per_tensor;
-             i += (int64_t)gridDim.x * kThreads) {
-            const uint4 qa = a[t * vec_per_tensor + i], qb = b[t * vec_per_tensor + i];
-            if (((qa.x ^ qb.x) | (qa.y ^ qb.y) | (qa.z ^ qb.z) | (qa.w ^ qb.w)) == 0u)
-                continue;
-            count_word(qa.x, qb.x, mism, adj);
-            count_word(qa.y, qb.y, mism, adj);
-            count_word(qa.z, qb.z, mism, adj);
-            count_word(qa.w, qb.w, mism, adj);
+             i += kMismatchUnroll * stride) {
+            uint4 qa[kMismatchUnroll], qb[kMismatchUnroll];
+#pragma unroll
+            for (int u = 0; u < kMismatchUnroll; ++u) {
+                const int64_t j = i + u * stride < last ? i + u * stride : last;
+                qa[u] = ta[j];
+                qb[u] = tb[j];
+            }
+#pragma unroll
+            for (int u = 0; u < kMismatchUnroll; ++u)
+                if (i + u * stride < vec_per_tensor)
+                    count_vec(qa[u], qb[u], mism, adj);
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) {
@@ -529,7 +558,8 @@ void launch_mismatch(const uint8_t* a, const uint8_t* b, int64_t batch, int64_t 
     const int64_t vec = per_tensor / 32;
     if (vec == 0)
         return;
-    dim3 grid(groups_per_tensor(vec, batch, kQuantGroups), grid_y(batch));
+    const unsigned gx = groups_per_tensor((vec + kMismatchUnroll - 1) / kMismatchUnroll, batch, kQuantGroups);
+    dim3 grid(gx < kMismatchMaxGroups ? gx : kMismatchMaxGroups, grid_y(batch));
     hipLaunchKernelGGL(mismatch_kernel, grid, dim3(kThreads), 0, s,
                        reinterpret_cast<const uint4*>(a), reinterpret_cast<const uint4*>(b), vec,
                        batch, reinterpret_cast<unsigned long long*>(counts));

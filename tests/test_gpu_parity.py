@@ -1054,6 +1054,28 @@ def test_w4a4_gemm_mid_size(counts, n, k):
     _w4a4_check(counts, n, k, seed=11, sample=64, strict=False)
 
 
+@pytest.mark.parametrize("batch,per", [(3, 32 * (2 ** 20 + 7)), (64, 32 * 6149), (5, 32 * 9)])
+def test_code_mismatch_ragged_and_capped(batch, per):
+    """Mismatch counts over sizes that reach every path of the counting loop: pair
+    counts (16 bytes of codes each) that leave a ragged last pass, whose extra loads
+    are clamped to the last pair and not counted; a tensor of 2^20 + 7 pairs, more than
+    its capped number of workgroups covers in one pass; several tensors per launch.
+    Bit-exact against the oracle."""
+    rng = np.random.default_rng(batch)
+    a = rng.integers(0, 256, batch * per // 2, dtype=np.uint8)
+    b = a.copy()
+    flip = rng.random(b.size) < 0.01
+    b[flip] ^= rng.integers(1, 256, int(flip.sum()), dtype=np.uint8)
+    # the last pair of every tensor differs, so that a clamped load counted twice would show
+    last = np.arange(1, batch + 1) * (per // 2) - 1
+    b[last] = a[last] ^ 0x11
+    got = ops.code_mismatch(torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV), batch, per)
+    torch.cuda.synchronize()
+    want = oracle.code_mismatch(a, b, batch, per)
+    assert np.array_equal(got.cpu().numpy().astype(np.uint64), want)
+    assert (want[:, 0] > 0).all()
+
+
 def test_code_mismatch_random():
     rng = np.random.default_rng(3)
     B, per = 5, 4096
