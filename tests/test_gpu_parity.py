@@ -263,9 +263,9 @@ def test_amax_given_and_tensor_amax():
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_quantize_more_tensors_than_grid_rows(dtype):
     """65541 tensors of 2 x 16 values: more tensors than the launch has workgroup rows
-    (65535), so the quantizers take their looping path over tensors.  Nearest with
-    hints, guided and from-scratch amax, bit-exact against the oracle on every
-    tensor."""
+    (65535), so the quantizers and the mismatch count take their looping path over
+    tensors.  Nearest with hints, guided, from-scratch amax and the per-tensor
+    mismatch counts, bit-exact against the oracle on every tensor."""
     B, R, Cc = 65541, 2, 16
     rng = np.random.default_rng(65541)
     x = (rng.standard_normal((B, R, Cc)) * np.exp2(rng.integers(-20, 20, (B, 1, 1)))).astype(np.float32)
@@ -284,7 +284,17 @@ def test_quantize_more_tensors_than_grid_rows(dtype):
     assert_q_equal(qr, o_r, "rollout")
     o_h = oracle.extract_hint(o_r["codes"], n)
     assert np.array_equal(hints_np(hints), o_h)
-    assert_q_equal(qg, oracle.quantize_guided(gt, B, R, Cc, o_h), "guided")
+    o_g = oracle.quantize_guided(gt, B, R, Cc, o_h)
+    assert_q_equal(qg, o_g, "guided")
+    # guided codes match the rollout's here, so count against the trainer's nearest codes
+    qn = ops.quantize(gt.to(DEV))
+    cnt = ops.code_mismatch(qr.codes.reshape(-1), qn.codes.reshape(-1), B, R * Cc)
+    torch.cuda.synchronize()
+    o_n = oracle.quantize(gt, B, R, Cc)
+    assert_q_equal(qn, o_n, "trainer nearest")
+    want = oracle.code_mismatch(o_r["codes"].reshape(-1), o_n["codes"].reshape(-1), B, R * Cc)
+    assert want[:, 0].sum() > 0
+    assert np.array_equal(cnt.cpu().numpy().astype(np.uint64), want)
 
 
 def test_empty_tensors():
