@@ -65,10 +65,18 @@ constexpr int kNJ = 2;                            // MFMA tiles per wave along N
 
 constexpr int kCP = 64 + 4;                       // bf16 per staged output row of one wave
 
+// Activation tiles in LDS: a ring of three with bf16 activations (slice t + 1
+// is complete before slice t ends, so its first fragments are read before the
+// barrier); two with NVFP4 activations, whose staged activation scales leave no
+// room for a third tile at two workgroups per CU, and two without staged scales
+// (the per-slice scale registers leave none for the early fragments).
+template <bool A_FP4, bool SLDS>
+constexpr int ring() { return A_FP4 || !SLDS ? 2 : 3; }
+
 template <bool A_FP4, bool SLDS>
 constexpr int smem_bytes()
 {
-    const int ops = 2 * kATile + (SLDS ? kWSTile + (A_FP4 ? kASTile : 0) : 0);
+    const int ops = ring<A_FP4, SLDS>() * kATile + (SLDS ? kWSTile + (A_FP4 ? kASTile : 0) : 0);
     const int out = 4 * kBM * kCP * 2;  // each wave's staged 128 x 64 output block
     return ops > out ? ops : out;
 }
@@ -132,8 +140,9 @@ __global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
     // Two activation tiles (the one being read, the one being filled), then the
     // staged scales; the output tile is staged over the same bytes.
     __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<A_FP4, SLDS>()];
-    uint8_t* const Ws = smem + 2 * kATile;            // weight scales [kBN][K/16]
-    uint8_t* const As_s = smem + 2 * kATile + kWSTile;  // activation scales [kBM][K/16]
+    constexpr int kRing = ring<A_FP4, SLDS>();
+    uint8_t* const Ws = smem + kRing * kATile;              // weight scales [kBN][K/16]
+    uint8_t* const As_s = smem + kRing * kATile + kWSTile;  // activation scales [kBM][K/16]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -417,14 +426,36 @@ __global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
 
     ARegs<A_FP4> RA;
     WRegs S0, S1, S2 = {};
-    uint32_t sc[kNJ] = {};  // SLDS: weight scale bytes of the slice about to run
+    // Decoded weight scales of the slice whose fragments are being produced.
+    // The first fragments of slice t + 1 are produced at the end of slice t
+    // (before its barrier), so that slice t + 1 opens with its MFMAs.
+    f32x2_t dcur[kNJ];
+    bf16x8_t bf_ring[2][kNJ], af_ring[2][kNI];
+    auto afrag = [&](const uint8_t* Ab, int i, int kk) -> bf16x8_t {
+        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
+            Ab + swz(32 * i + (lane & 31), 4 * h + kk)));
+    };
+    auto word = [&](const WRegs& R, int j, int kk) -> uint32_t {
+        return kk == 0 ? R.w[j].x : (kk == 1 ? R.w[j].y : (kk == 2 ? R.w[j].z : R.w[j].w));
+    };
+    // weight scale bytes of slice t for column j (staged or in the slice's registers)
+    auto wsc = [&](const WRegs& R, int j, int t) -> uint32_t {
+        if constexpr (SLDS)
+            return lds_wscales(j, t < steps ? t : steps - 1);
+        else
+            return R.s[j];
+    };
     if (steps > 0) {
+        // slice 0 (and with a ring of three, slice 1) into the first LDS tiles
+        ARegs<A_FP4> RA1;
         if (r_tail) {
             load_partial(RA, S0);
         } else {
             load_a(0, RA);
             load_w(0, S0);
         }
+        if constexpr (kRing == 3)
+            load_a(1, RA1);
         load_w(1, S1);
         if constexpr (SLDS) {
             copy_scales(rs_s, w_rows * kb, Ws, std::integral_constant<int, kWSTile>{}, sw_l2d);
@@ -434,62 +465,86 @@ __global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
             }
         }
         store_a(RA, 0, smem);
+        if constexpr (kRing == 3)
+            store_a(RA1, 1, smem + kATile);
     }
     __syncthreads();
-    if constexpr (SLDS) {
-        if (steps > 0) {
+    const int nl_all = (int)((row_end - row0 + 31) / 32);  // live 32-row blocks (the tile's rows)
+    if (kRing == 3 && steps > 0) {
 #pragma unroll
-            for (int j = 0; j < kNJ; ++j) {
-                sc[j] = lds_wscales(j, 0);
-                if (r_tail)
-                    sc[j] = mask_partial(sc[j], h);
-            }
+        for (int j = 0; j < kNJ; ++j) {
+            uint32_t s0 = wsc(S0, j, 0);
+            if (r_tail)
+                s0 = mask_partial(s0, h);
+            dcur[j] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(s0, 1.0f, false);
+            bf_ring[0][j] = __builtin_bit_cast(bf16x8_t, dequant8_bf16(word(S0, j, 0), dcur[j][0]));
         }
+#pragma unroll
+        for (int i = 0; i < kNI; ++i)
+            if (i < nl_all)
+                af_ring[0][i] = afrag(smem, i, 0);
     }
     // One slice with NL live 32-row blocks (blocks past the group's end only feed
-    // rows that are never stored, so their MFMAs are skipped).  `cur` holds the
-    // codes of slice t, `nxt` receives those of t + 2.
-    auto step = [&](auto nl, int t, const WRegs& cur, WRegs& nxt) __attribute__((always_inline)) {
+    // rows that are never stored, so their MFMAs are skipped).  On entry the
+    // fragments of its first MFMA step are in bf[0] / af[0]; `cur` holds its
+    // codes, `nx1` those of t + 1, and `nxt` receives those of t + 2.  Slice t
+    // reads LDS tile t % kRing.  With three tiles the activations of t + 2 go into
+    // tile (t + 2) % 3, which slice t - 1 read before the previous barrier, and
+    // tile (t + 1) % 3 is read for slice t + 1's first step before this slice's
+    // barrier.  With two, the activations of t + 1 go into tile (t + 1) % 2 and
+    // are read after the barrier.
+    auto step = [&](auto nl, int t, const WRegs& cur, const WRegs& nx1, WRegs& nxt) __attribute__((always_inline)) {
         constexpr int NL = decltype(nl)::value;
-        load_a(t + 1, RA);
+        // with two tiles the fragments live only within the slice
+        bf16x8_t bfl[2][kNJ], afl[2][kNI];
+        bf16x8_t(&bf)[2][kNJ] = *(kRing == 3 ? &bf_ring : &bfl);
+        bf16x8_t(&af)[2][kNI] = *(kRing == 3 ? &af_ring : &afl);
+        load_a(t + kRing - 1, RA);
         load_w(t + 2, nxt);
         __builtin_amdgcn_sched_barrier(0);  // keep the loads at the top of the slice
-        const uint8_t* Ac = smem + kATile * (t & 1);
-        f32x2_t d[kNJ];
-#pragma unroll
-        for (int j = 0; j < kNJ; ++j)
-            d[j] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(SLDS ? sc[j] : cur.s[j], 1.0f, false);
-        if constexpr (SLDS) {
-            // next slice's weight scales (past the last slice: of no consequence)
+        const int b0 = t % kRing, b1 = b0 == kRing - 1 ? 0 : b0 + 1, b2 = b1 == kRing - 1 ? 0 : b1 + 1;
+        const uint8_t* Ac = smem + kATile * b0;
+        const uint8_t* An = smem + kATile * b1;
+        uint32_t snext[kNJ];  // three tiles: scale bytes of slice t + 1, decoded at the last step
+        if constexpr (kRing == 3) {
 #pragma unroll
             for (int j = 0; j < kNJ; ++j)
-                sc[j] = lds_wscales(j, t + 1 < steps ? t + 1 : t);
+                snext[j] = wsc(nx1, j, t + 1);
+        } else {
+            // two tiles: this slice's first fragments, from the tile completed at
+            // the previous barrier
+#pragma unroll
+            for (int j = 0; j < kNJ; ++j) {
+                uint32_t st = wsc(cur, j, t);
+                if (SLDS && t == 0 && r_tail)  // staged scales of blocks past K % 64
+                    st = mask_partial(st, h);
+                dcur[j] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(st, 1.0f, false);
+                bf[0][j] = __builtin_bit_cast(bf16x8_t, dequant8_bf16(word(cur, j, 0), dcur[j][0]));
+            }
+#pragma unroll
+            for (int i = 0; i < NL; ++i)
+                af[0][i] = afrag(Ac, i, 0);
         }
-        auto word = [&](int j, int kk) -> uint32_t {
-            return kk == 0 ? cur.w[j].x : (kk == 1 ? cur.w[j].y : (kk == 2 ? cur.w[j].z : cur.w[j].w));
-        };
-        auto afrag = [&](int i, int kk) -> bf16x8_t {
-            return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(
-                Ac + swz(32 * i + (lane & 31), 4 * h + kk)));
-        };
-        bf16x8_t bf[2][kNJ], af[2][kNI];
-#pragma unroll
-        for (int j = 0; j < kNJ; ++j)
-            bf[0][j] = __builtin_bit_cast(bf16x8_t, dequant8_bf16(word(j, 0), d[j][0]));
-#pragma unroll
-        for (int i = 0; i < NL; ++i)
-            af[0][i] = afrag(i, 0);
 #pragma unroll
         for (int kk = 0; kk < kBK / 16; ++kk) {
             const int c = kk & 1, nx = c ^ 1;
-            if (kk + 1 < kBK / 16) {
+            // fragments of the next MFMA step: step kk + 1 of this slice, or step 0
+            // of slice t + 1 (tile b1 was complete at the previous barrier)
+            const bool last = kk + 1 == kBK / 16;
+            if (!last || kRing == 3) {
 #pragma unroll
                 for (int i = 0; i < NL; ++i)
-                    af[nx][i] = afrag(i, kk + 1);
+                    af[nx][i] = last ? afrag(An, i, 0) : afrag(Ac, i, kk + 1);
+                if (last) {
+#pragma unroll
+                    for (int j = 0; j < kNJ; ++j)
+                        dcur[j] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(snext[j], 1.0f, false);
+                }
 #pragma unroll
                 for (int j = 0; j < kNJ; ++j)
                     bf[nx][j] = __builtin_bit_cast(
-                        bf16x8_t, dequant8_bf16(word(j, kk + 1), d[j][(kk + 1) >> 1]));
+                        bf16x8_t, dequant8_bf16(last ? word(nx1, j, 0) : word(cur, j, kk + 1),
+                                                dcur[j][last ? 0 : (kk + 1) >> 1]));
             }
 #pragma unroll
             for (int i = 0; i < NL; ++i)
@@ -503,30 +558,31 @@ __global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
                 // step to land and the dequantization runs between MFMAs.  (The
                 // per-slice scale loads of the other instantiation leave no
                 // registers for this order.)
-                if (kk + 1 < kBK / 16)
+                const bool pre = !last || kRing == 3;
+                if (pre)
                     __builtin_amdgcn_sched_group_barrier(0x100, NL, 0);  // LDS reads
 #pragma unroll
                 for (int m = 0; m < NL * kNJ; ++m) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                    if (kk + 1 < kBK / 16)
+                    if (pre)
                         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // activations of slice t + 1 into the other tile (zeros past the last
-        // slice, into a tile nobody reads again)
-        store_a(RA, t + 1, smem + kATile * (1 - (t & 1)));
+        // activations of slice t + kRing - 1 into the tile after this one's
+        // successor (zeros past the last slice, into a tile nobody reads again)
+        store_a(RA, t + kRing - 1, smem + kATile * (kRing == 3 ? b2 : b1));
         __syncthreads();
     };
     // three slices per trip so that the three code register sets rotate without copies
     auto run = [&](auto nl) __attribute__((always_inline)) {
         for (int t = 0; t < steps; t += 3) {
-            step(nl, t, S0, S2);
+            step(nl, t, S0, S1, S2);
             if (t + 1 < steps)
-                step(nl, t + 1, S1, S0);
+                step(nl, t + 1, S1, S2, S0);
             if (t + 2 < steps)
-                step(nl, t + 2, S2, S1);
+                step(nl, t + 2, S2, S0, S1);
         }
     };
     const int64_t live_rows = row_end - row0;
