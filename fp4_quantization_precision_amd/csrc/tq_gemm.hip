@@ -35,10 +35,14 @@
 // 16-byte loads and read from LDS in the loop; otherwise they are loaded two
 // bytes per lane and slice.
 //
-// Pipeline.  During K-slice t the activations of slice t + 1 and the weight
-// codes of slice t + 2 are in flight (three code register sets rotate); the
-// activations are written to the other of two LDS tiles at the end of the
-// slice, so one barrier per slice suffices.  The fragments of MFMA step kk + 1
+// Pipeline.  The weight codes of slice t + 2 are in flight during K-slice t
+// (three code register sets rotate).  With bf16 activations and staged scales
+// the activation tiles form a ring of three in LDS: the activations of slice
+// t + 2 are loaded during slice t and written at its end into the tile slice
+// t - 1 read, so slice t + 1's tile is complete before slice t ends and the
+// first fragments of slice t + 1 are produced before the barrier.  Otherwise
+// two tiles alternate and slice t + 1's activations are loaded during slice t.
+// Either way one barrier per slice suffices.  The fragments of MFMA step kk + 1
 // (weights dequantized, activations read) are produced while the MFMAs of step
 // kk run, in a fixed issue order: the fragment reads first, then one MFMA per
 // four dequantization VALU instructions.  All operand loads are buffer loads against per-workgroup resources:
@@ -137,8 +141,8 @@ __global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
     const uint8_t* __restrict__ w_scales, const float* __restrict__ w_tensor_scale,
     uint16_t* __restrict__ out, int n_tiles, int sw_l2d)
 {
-    // Two activation tiles (the one being read, the one being filled), then the
-    // staged scales; the output tile is staged over the same bytes.
+    // The ring of activation tiles, then the staged scales; the output tile is
+    // staged over the same bytes.
     __shared__ __attribute__((aligned(16))) uint8_t smem[smem_bytes<A_FP4, SLDS>()];
     constexpr int kRing = ring<A_FP4, SLDS>();
     uint8_t* const Ws = smem + kRing * kATile;              // weight scales [kBN][K/16]
@@ -485,9 +489,10 @@ __global__ __launch_bounds__(kGThreads, 2) void grouped_gemm_nvfp4_kernel(
                 af_ring[0][i] = afrag(smem, i, 0);
     }
     // One slice with NL live 32-row blocks (blocks past the group's end only feed
-    // rows that are never stored, so their MFMAs are skipped).  On entry the
-    // fragments of its first MFMA step are in bf[0] / af[0]; `cur` holds its
-    // codes, `nx1` those of t + 1, and `nxt` receives those of t + 2.  Slice t
+    // rows that are never stored, so their MFMAs are skipped).  With three tiles
+    // the fragments of its first MFMA step are in bf[0] / af[0] on entry; with two
+    // they are produced at the top of the slice.  `cur` holds its codes, `nx1`
+    // those of t + 1, and `nxt` receives those of t + 2.  Slice t
     // reads LDS tile t % kRing.  With three tiles the activations of t + 2 go into
     // tile (t + 2) % 3, which slice t - 1 read before the previous barrier, and
     // tile (t + 1) % 3 is read for slice t + 1's first step before this slice's
