@@ -1064,6 +1064,37 @@ def test_w4a4_gemm_mid_size(counts, n, k):
     _w4a4_check(counts, n, k, seed=11, sample=64, strict=False)
 
 
+def test_grouped_gemms_repeatable():
+    """Every output element of the full-size GEMMs, bit for bit, over repeated calls
+    with the launches of other shapes in between.  The accumulation order is fixed
+    by the kernel, so any difference between calls would come from a race on the
+    activation tiles in LDS (written for a later slice while an earlier one is still
+    read) or on the output staging."""
+    shapes = [(inputs.zipf_counts(64, 16384, 1.1), 2048, 768),   # three LDS tiles
+              (inputs.zipf_counts(32, 16384, 1.1), 768, 2048),   # three LDS tiles
+              ([300, 1, 129, 700], 136, 784),                    # partial first slice
+              ([64] * 5, 256, 2064)]                             # per-slice scale loads
+    calls = []
+    for i, (counts, n, k) in enumerate(shapes):
+        G, M = len(counts), int(sum(counts))
+        a, w, off = inputs.grouped_gemm_inputs(groups=G, tokens=M, k=k, n=n, device=DEV,
+                                               seed=20 + i, counts=counts)
+        wq = ops.quantize(w)  # [G, n, k]: one tensor scale per expert
+        aq = ops.quantize(a)  # [M, k]: one tensor
+        offd = off.to(DEV)
+        calls.append((lambda a=a, offd=offd, wq=wq, n=n, k=k: ops.grouped_gemm_nvfp4(a, offd, wq, n, k),
+                      f"bf16 {G}x[{M}x{k}x{n}]"))
+        calls.append((lambda aq=aq, offd=offd, wq=wq, n=n, k=k: ops.grouped_gemm_w4a4(aq, offd, wq, n, k),
+                      f"W4A4 {G}x[{M}x{k}x{n}]"))
+    first = [f().view(torch.int16).clone() for f, _ in calls]
+    torch.cuda.synchronize()
+    for rep in range(6):
+        for (f, name), ref in zip(calls if rep % 2 == 0 else calls[::-1],
+                                  first if rep % 2 == 0 else first[::-1]):
+            out = f()
+            assert torch.equal(out.view(torch.int16), ref), f"{name}: call {rep + 2} differs"
+
+
 @pytest.mark.parametrize("batch,per", [(3, 32 * (2 ** 20 + 7)), (64, 32 * 6149), (5, 32 * 9)])
 def test_code_mismatch_ragged_and_capped(batch, per):
     """Mismatch counts over sizes that reach every path of the counting loop: pair
